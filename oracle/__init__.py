@@ -1,0 +1,151 @@
+"""CPU oracle of the GDN speculative-decode state update -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding) never imports, links or calls anything here, and nothing
+here imports the product package.
+
+The arithmetic lives in ``gdn_oracle.c`` (plain serial C, every operation in
+double); this module only marshals torch/numpy arrays into it:
+inputs of any float dtype are upcast exactly to float64, the C code rounds to
+the storage format at each slot/output write, and the results are cast back
+to the caller's dtypes (exact, because the values are already representable).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gdn_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+FMT_F32, FMT_F16, FMT_BF16, FMT_F64 = 0, 1, 2, 3
+_FMT = {torch.float32: FMT_F32, torch.float16: FMT_F16,
+        torch.bfloat16: FMT_BF16, torch.float64: FMT_F64}
+_ERR = {1: "bad argument", 2: "index out of range", 3: "out of memory"}
+
+_lib = None
+
+
+def build() -> str:
+    """Compile liboracle.so with gcc (no FMA contraction, no fast-math)."""
+    tmp = _LIB_PATH + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-ffp-contract=off",
+           "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    d, i32, i64, vp = ctypes.c_double, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+    lib.orc_round.restype = d
+    lib.orc_round.argtypes = [ctypes.c_int, d]
+    common_head = [vp] * 9 + [vp, ctypes.c_int, vp, ctypes.c_int, i64, i64]
+    lib.orc_spec_update.restype = ctypes.c_int
+    lib.orc_spec_update.argtypes = common_head + [vp, i32, vp, i64, vp, vp,
+                                                  i32, i32, i32, i32, d, d]
+    lib.orc_decode_update.restype = ctypes.c_int
+    lib.orc_decode_update.argtypes = common_head + [vp, i32, vp,
+                                                    i32, i32, i32, i32, d, d]
+    _lib = lib
+    return lib
+
+
+def round_to(dtype: torch.dtype, x) -> np.ndarray:
+    """Element-wise orc_round (nearest, ties to even) into ``dtype``'s format."""
+    lib = _load()
+    fmt = _FMT[dtype]
+    xs = np.asarray(x, dtype=np.float64).ravel()
+    return np.array([lib.orc_round(fmt, float(e)) for e in xs]).reshape(np.shape(x))
+
+
+def _f64(t) -> np.ndarray:
+    if isinstance(t, torch.Tensor):
+        return np.ascontiguousarray(t.detach().cpu().to(torch.float64).numpy())
+    return np.ascontiguousarray(np.asarray(t, dtype=np.float64))
+
+
+def _i32(t):
+    if t is None:
+        return None
+    if isinstance(t, torch.Tensor):
+        t = t.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(t, dtype=np.int32))
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _prepare(q, k, v, z, a, b, A_log, dt_bias, norm_weight, pool, out, out_dtype):
+    n_tok, HK, K = q.shape
+    HV, V = v.shape[1], v.shape[2]
+    assert k.shape == (n_tok, HK, K) and z.shape == (n_tok, HV, V)
+    assert a.shape == (n_tok, HV) and b.shape == (n_tok, HV)
+    assert pool.shape[1:] == (HV, V, K)
+    if out is None:
+        out = torch.zeros((n_tok, HV, V), dtype=out_dtype or z.dtype)
+    arrs = [_f64(x) for x in (q, k, v, z, a, b, A_log, dt_bias, norm_weight)]
+    # pool and out are written by the C code: always work on private copies
+    return (arrs, _f64(out).copy(), out.dtype, _f64(pool).copy(),
+            (n_tok, HK, HV, K, V))
+
+
+def spec_update(q, k, v, z, a, b, A_log, dt_bias, norm_weight, pool,
+                cu_seqlens, spec_state_indices, num_accepted_tokens, *,
+                token_indx=None, out=None, out_dtype=None, scale=None,
+                norm_eps=1e-5):
+    """Speculative update; returns ``(pool_after, out_after)`` as new tensors.
+
+    ``pool`` is ``[num_slots, HV, V, K]``; ``spec_state_indices`` is
+    ``[B, spec_stride]``; ``out`` (default zeros) supplies the rows that are
+    not processed.  Inputs are not modified.
+    """
+    arrs, out64, odt, pool64, (n_tok, HK, HV, K, V) = _prepare(
+        q, k, v, z, a, b, A_log, dt_bias, norm_weight, pool, out, out_dtype)
+    cu = _i32(cu_seqlens)
+    si = _i32(spec_state_indices)
+    na = _i32(num_accepted_tokens)
+    ti = _i32(token_indx)
+    B = cu.shape[0] - 1
+    stride = si.shape[1] if si.ndim == 2 else max(1, si.shape[0] // max(B, 1))
+    scale = K ** -0.5 if scale is None else scale
+    rc = _load().orc_spec_update(
+        *[_p(x) for x in arrs], _p(out64), _FMT[odt], _p(pool64), _FMT[pool.dtype],
+        pool.shape[0], n_tok, _p(cu), B, _p(si), stride, _p(na), _p(ti),
+        HK, HV, K, V, float(scale), float(norm_eps))
+    if rc:
+        raise ValueError(f"oracle spec_update: {_ERR.get(rc, rc)}")
+    return (torch.from_numpy(pool64).to(pool.dtype),
+            torch.from_numpy(out64).to(odt))
+
+
+def decode_update(q, k, v, z, a, b, A_log, dt_bias, norm_weight, pool,
+                  state_indices, *, token_indx=None, out=None, out_dtype=None,
+                  scale=None, norm_eps=1e-5):
+    """Non-speculative single-token in-place update; returns new tensors."""
+    arrs, out64, odt, pool64, (n_tok, HK, HV, K, V) = _prepare(
+        q, k, v, z, a, b, A_log, dt_bias, norm_weight, pool, out, out_dtype)
+    si = _i32(state_indices)
+    ti = _i32(token_indx)
+    scale = K ** -0.5 if scale is None else scale
+    rc = _load().orc_decode_update(
+        *[_p(x) for x in arrs], _p(out64), _FMT[odt], _p(pool64), _FMT[pool.dtype],
+        pool.shape[0], n_tok, _p(si), si.shape[0], _p(ti),
+        HK, HV, K, V, float(scale), float(norm_eps))
+    if rc:
+        raise ValueError(f"oracle decode_update: {_ERR.get(rc, rc)}")
+    return (torch.from_numpy(pool64).to(pool.dtype),
+            torch.from_numpy(out64).to(odt))

@@ -1,0 +1,243 @@
+"""Seeded synthetic inputs for the GDN speculative-decode update.
+
+This module holds no arithmetic of the method: it only draws random numbers
+and lays out metadata.  Tests, the benchmark and the smoke check all take
+their inputs from here, so the GPU path and the CPU oracle always see the
+same bytes.
+
+Recipe (one ``numpy.random.Generator(PCG64(seed))`` per batch, drawn in this
+order): q, k, v, z, a, b (standard normal, fp32), A_log ~ U(-1, 1),
+dt_bias ~ U(-0.5, 0.5), norm_weight ~ U(0.5, 1.5), the state pool (normal
+with the stated deviation, drawn slot by slot), the slot permutation,
+num_accepted_tokens, and for mixed batches the order of the units.  Every
+value is drawn in fp32 and rounded to nearest-even into its stated dtype.
+
+The shapes follow the decode workloads on the vLLM PR reports: K = V = 128,
+grouped heads HV = G * HK, at most 8 draft tokens per sequence, a state pool
+of ``[num_slots, HV, V, K]`` with one slot per (sequence, draft token).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+import torch
+
+_DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@dataclass
+class GDNBatch:
+    """One layer's worth of decode inputs (CPU tensors)."""
+    name: str
+    HK: int
+    HV: int
+    K: int
+    V: int
+    q: torch.Tensor            # [n_tok, HK, K]
+    k: torch.Tensor            # [n_tok, HK, K]
+    v: torch.Tensor            # [n_tok, HV, V]
+    z: torch.Tensor            # [n_tok, HV, V]  output gate
+    a: torch.Tensor            # [n_tok, HV]
+    b: torch.Tensor            # [n_tok, HV]
+    A_log: torch.Tensor        # [HV] fp32
+    dt_bias: torch.Tensor      # [HV] fp32
+    norm_weight: torch.Tensor  # [V] fp32
+    pool: torch.Tensor         # [num_slots, HV, V, K]
+    out_dtype: torch.dtype
+    # speculative part (B sequences, row space of the spec call)
+    cu_seqlens: torch.Tensor            # int32 [B+1]
+    spec_state_indices: torch.Tensor    # int32 [B, T]
+    num_accepted_tokens: torch.Tensor   # int32 [B]
+    spec_token_indx: Optional[torch.Tensor] = None   # int32 [cu[B]] or None
+    # non-speculative part (single-token, in-place)
+    state_indices: Optional[torch.Tensor] = None     # int32 [N_ns]
+    non_spec_token_indx: Optional[torch.Tensor] = None
+    T: int = 0
+    scale: float = field(default=0.0)
+    norm_eps: float = 1e-5
+
+    @property
+    def n_tok(self) -> int:
+        return self.q.shape[0]
+
+    @property
+    def num_seqs(self) -> int:
+        return self.cu_seqlens.shape[0] - 1
+
+    @property
+    def num_non_spec(self) -> int:
+        return 0 if self.state_indices is None else self.state_indices.shape[0]
+
+    def spec_rows(self) -> int:
+        return int(self.cu_seqlens[-1])
+
+    def draft_tokens(self) -> int:
+        """Rows processed by one step: spec rows plus non-spec entries."""
+        ns = 0 if self.state_indices is None else int((self.state_indices >= 0).sum())
+        return self.spec_rows() + ns
+
+    def algorithmic_bytes(self) -> int:
+        """Bytes one step must move: each active sequence reads its state once
+        and writes one tile per token; each non-spec entry reads and writes one
+        tile; every processed row moves q, k (per key head), v, z, out (per
+        value head) and the two gate scalars; plus metadata and parameters."""
+        s_state = self.pool.element_size()
+        s_act = self.q.element_size()
+        s_out = torch.empty((), dtype=self.out_dtype).element_size()
+        tile = self.HV * self.K * self.V * s_state
+        lens = (self.cu_seqlens[1:] - self.cu_seqlens[:-1]).clamp(min=0)
+        active = lens > 0
+        state = int(((1 + lens) * active).sum()) * tile
+        ns = 0 if self.state_indices is None else int((self.state_indices >= 0).sum())
+        state += 2 * ns * tile
+        rows = self.draft_tokens()
+        per_row = (2 * self.HK * self.K * s_act
+                   + self.HV * self.V * (2 * s_act + s_out)
+                   + 2 * self.HV * s_act)
+        meta = 4 * (self.cu_seqlens.numel() + self.num_accepted_tokens.numel()
+                    + int(active.sum()) * (self.T + 1))
+        if self.spec_token_indx is not None:
+            meta += 4 * self.spec_token_indx.numel()
+        if self.state_indices is not None:
+            meta += 4 * 2 * self.state_indices.numel()
+        params = 4 * (2 * self.HV + self.V)
+        return state + rows * per_row + meta + params
+
+
+def _draw_act(rng, shape, dtype):
+    x = rng.standard_normal(shape, dtype=np.float32)
+    return torch.from_numpy(x).to(dtype)
+
+
+def _draw_pool(rng, num_slots, HV, V, K, std, dtype):
+    pool = torch.empty((num_slots, HV, V, K), dtype=dtype)
+    for s in range(num_slots):
+        x = rng.standard_normal((HV, V, K), dtype=np.float32) * np.float32(std)
+        pool[s] = torch.from_numpy(x).to(dtype)
+    return pool
+
+
+def _common(rng, n_tok, HK, HV, K, V, act, num_slots, pool_std, state):
+    q = _draw_act(rng, (n_tok, HK, K), act)
+    k = _draw_act(rng, (n_tok, HK, K), act)
+    v = _draw_act(rng, (n_tok, HV, V), act)
+    z = _draw_act(rng, (n_tok, HV, V), act)
+    a = _draw_act(rng, (n_tok, HV), act)
+    b = _draw_act(rng, (n_tok, HV), act)
+    A_log = torch.from_numpy(rng.uniform(-1.0, 1.0, HV).astype(np.float32))
+    dt_bias = torch.from_numpy(rng.uniform(-0.5, 0.5, HV).astype(np.float32))
+    norm_weight = torch.from_numpy(rng.uniform(0.5, 1.5, V).astype(np.float32))
+    pool = _draw_pool(rng, num_slots, HV, V, K, pool_std, state)
+    return q, k, v, z, a, b, A_log, dt_bias, norm_weight, pool
+
+
+def spec_batch(*, B, T, HK, HV, K=128, V=128, act="bf16", state="bf16",
+               out=None, num_slots=None, pool_std=0.05, acc_lo=0, acc_hi=None,
+               q_lens=None, seed=0, name="spec") -> GDNBatch:
+    """A pure speculative batch: B sequences of up to T draft tokens each.
+
+    ``q_lens`` (default: all T) gives each sequence's row count; rows are laid
+    out contiguously in sequence order.  ``spec_state_indices`` is a random
+    permutation of the pool's slots reshaped to ``[B, T]`` (the first B*T
+    entries when the pool is larger); num_accepted ~ U{acc_lo..acc_hi}.
+    """
+    acc_hi = T if acc_hi is None else acc_hi
+    num_slots = B * T if num_slots is None else num_slots
+    assert num_slots >= B * T
+    lens = np.full(B, T, dtype=np.int64) if q_lens is None else np.asarray(q_lens, np.int64)
+    assert lens.shape == (B,) and (lens <= T).all()
+    cu = np.zeros(B + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(np.maximum(lens, 0))
+    n_tok = int(cu[-1])
+    rng = np.random.Generator(np.random.PCG64(seed))
+    act_t, state_t = _DT[act], _DT[state]
+    q, k, v, z, a, b, A_log, dt_bias, w, pool = _common(
+        rng, n_tok, HK, HV, K, V, act_t, num_slots, pool_std, state_t)
+    perm = rng.permutation(num_slots).astype(np.int32)
+    acc = rng.integers(acc_lo, acc_hi + 1, size=B).astype(np.int32)
+    return GDNBatch(
+        name=name, HK=HK, HV=HV, K=K, V=V, q=q, k=k, v=v, z=z, a=a, b=b,
+        A_log=A_log, dt_bias=dt_bias, norm_weight=w, pool=pool,
+        out_dtype=_DT[out or act], cu_seqlens=torch.from_numpy(cu),
+        spec_state_indices=torch.from_numpy(perm[: B * T].reshape(B, T).copy()),
+        num_accepted_tokens=torch.from_numpy(acc), T=T, scale=K ** -0.5)
+
+
+def mixed_batch(*, n_non_spec, n_spec, T, HK, HV, K=128, V=128, act="bf16",
+                state="bf16", out=None, pool_std=0.05, acc_lo=0, acc_hi=None,
+                seed=0, name="mixed") -> GDNBatch:
+    """Non-spec single tokens and spec sequences of T rows, in random order.
+
+    The 'units' (singles and T-row blocks) are shuffled; rows are numbered in
+    unit order.  Spec sequences are numbered in the order they appear, so
+    ``spec_token_indx`` (their rows) is a non-identity gather index and
+    ``non_spec_token_indx`` holds the remaining rows.  The pool has one slot
+    per spec (sequence, token) plus one per non-spec entry, permuted.
+    """
+    acc_hi = T if acc_hi is None else acc_hi
+    n_tok = n_non_spec + n_spec * T
+    num_slots = n_tok
+    rng = np.random.Generator(np.random.PCG64(seed))
+    act_t, state_t = _DT[act], _DT[state]
+    q, k, v, z, a, b, A_log, dt_bias, w, pool = _common(
+        rng, n_tok, HK, HV, K, V, act_t, num_slots, pool_std, state_t)
+    perm = rng.permutation(num_slots).astype(np.int32)
+    acc = rng.integers(acc_lo, acc_hi + 1, size=n_spec).astype(np.int32)
+    order = rng.permutation(n_non_spec + n_spec)
+    spec_rows, ns_rows, row = [], [], 0
+    for u in order:
+        if u < n_non_spec:
+            ns_rows.append(row)
+            row += 1
+        else:
+            spec_rows.extend(range(row, row + T))
+            row += T
+    cu = np.arange(0, (n_spec + 1) * T, T, dtype=np.int32)
+    return GDNBatch(
+        name=name, HK=HK, HV=HV, K=K, V=V, q=q, k=k, v=v, z=z, a=a, b=b,
+        A_log=A_log, dt_bias=dt_bias, norm_weight=w, pool=pool,
+        out_dtype=_DT[out or act], cu_seqlens=torch.from_numpy(cu),
+        spec_state_indices=torch.from_numpy(perm[: n_spec * T].reshape(n_spec, T).copy()),
+        num_accepted_tokens=torch.from_numpy(acc),
+        spec_token_indx=torch.tensor(spec_rows, dtype=torch.int32),
+        state_indices=torch.from_numpy(perm[n_spec * T:].copy()),
+        non_spec_token_indx=torch.tensor(ns_rows, dtype=torch.int32),
+        T=T, scale=K ** -0.5)
+
+
+# The decode workloads.  C1 is the small case the oracle finishes at once;
+# C3b (B=128, T=8, BF16 state) is the headline measurement.
+CONFIGS = {
+    "C1": dict(kind="spec", B=2, T=3, HK=1, HV=8, act="f32", state="f32",
+               num_slots=8, pool_std=0.1, acc_lo=0, acc_hi=3, seed=0),
+    "C2": dict(kind="spec", B=32, T=4, HK=4, HV=32, act="bf16", state="bf16",
+               acc_lo=1, acc_hi=4, seed=2),
+    "C3": dict(kind="spec", B=128, T=8, HK=4, HV=32, act="bf16", state="f32",
+               acc_lo=0, acc_hi=8, seed=3),
+    "C3b": dict(kind="spec", B=128, T=8, HK=4, HV=32, act="bf16", state="bf16",
+                acc_lo=0, acc_hi=8, seed=3),
+    "C4": dict(kind="mixed", n_non_spec=64, n_spec=64, T=4, HK=4, HV=32,
+               act="bf16", state="bf16", acc_lo=0, acc_hi=4, seed=4),
+    "C5": dict(kind="spec", B=512, T=8, HK=16, HV=32, act="bf16", state="f16",
+               acc_lo=1, acc_hi=8, seed=5),
+}
+
+DESCRIPTIONS = {
+    "C1": "tiny spec step: B=2 T=3 HK=1 HV=8 K=V=128, fp32, 8-slot FP32 pool",
+    "C2": "MTP small batch: B=32 T=4 HK=4 HV=32 K=V=128, bf16, BF16 pool",
+    "C3": "MTP headline: B=128 T=8 HK=4 HV=32 K=V=128, bf16, FP32 pool, acc 0..8",
+    "C3b": "MTP headline: B=128 T=8 HK=4 HV=32 K=V=128, bf16, BF16 pool, acc 0..8",
+    "C4": "mixed: 64 non-spec T=1 + 64 spec T=4, HK=4 HV=32, bf16, BF16 pool",
+    "C5": "large batch: B=512 T=8 HK=16 HV=32 K=V=128, bf16, FP16 pool",
+}
+
+
+def make(name: str, **overrides) -> GDNBatch:
+    cfg = dict(CONFIGS[name])
+    cfg.update(overrides)
+    kind = cfg.pop("kind")
+    if kind == "mixed":
+        return mixed_batch(name=name, **cfg)
+    return spec_batch(name=name, **cfg)

@@ -1,0 +1,570 @@
+"""Pins of the CPU oracle against facts fixed by the PR reports and by the
+mathematics -- closed forms, special cases, invariants and a dense-matrix
+brute force -- so that a dropped term, a wrong sign or index, or a transposed
+operand in the oracle fails at least one of them.
+
+Page references are the vLLM PR reports on prhub.com.cn: #46090 (CPU DFlash
+spec decode for GDN: spec kernel excerpt), #51674 (fused CUDA post-conv MTP
+decode kernel: implementation breakdown item 1), #52191 (FP16/BF16 persisted
+GDN state: implementation breakdown item 4), #51812 (gate alignment under
+speculative gather: key source excerpt).
+"""
+import copy
+import itertools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from speculative_decode_amd import workloads
+from _helpers import (bitwise_equal, orc_decode, orc_spec, recover_o, rel_l2,
+                      silu, slots_touched, tiny, with_pool_dtype)
+
+F64 = torch.float64
+DTYPES = [torch.float32, torch.bfloat16, torch.float16, torch.float64]
+
+
+# --------------------------------------------------------------------------
+# Storage rounding (#52191: compute wide, store narrow).  Reduces to library
+# conversions: torch fp32->bf16 and numpy float64->float16 / ->float32 all
+# round to nearest even.
+# --------------------------------------------------------------------------
+def _rne_cases(seed=0):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal(4000) * np.exp2(rng.integers(-30, 30, 4000))
+    return x
+
+
+def test_round_f32_matches_numpy():
+    x = _rne_cases(1)
+    x = np.concatenate([x, [1e-46, -3e-45, 3.5e38, -3.41e38, 0.0, -0.0]])
+    got = oracle.round_to(torch.float32, x)
+    ref = x.astype(np.float32).astype(np.float64)
+    assert np.array_equal(got, ref)
+
+
+def test_round_f16_matches_numpy():
+    x = _rne_cases(2) * 1e-3
+    # subnormals, the overflow boundary (65520 rounds up to inf), exact ties
+    ties = np.array([1.0 + 2.0 ** -11, 1.0 + 3 * 2.0 ** -11, 2049.0, 2051.0,
+                     65519.99, 65520.0, -65520.0, 2.0 ** -25, 3 * 2.0 ** -25,
+                     1e-9, 6.0e-8])
+    x = np.concatenate([x, ties])
+    got = oracle.round_to(torch.float16, x)
+    ref = x.astype(np.float16).astype(np.float64)
+    assert np.array_equal(got, ref, equal_nan=True)
+
+
+def test_round_bf16_matches_torch():
+    # doubles that are exact fp32 values, so torch's fp32->bf16 is one rounding
+    x = _rne_cases(3).astype(np.float32).astype(np.float64)
+    ties = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 256.5, 257.5,
+                     2.0 ** -130, 3 * 2.0 ** -134, 3.3961e38])
+    x = np.concatenate([x, ties.astype(np.float32).astype(np.float64)])
+    got = oracle.round_to(torch.bfloat16, x)
+    ref = torch.from_numpy(x).to(torch.float32).to(torch.bfloat16).to(F64).numpy()
+    assert np.array_equal(got, ref)
+
+
+def test_round_special_values():
+    for dt in (torch.float32, torch.float16, torch.bfloat16):
+        r = oracle.round_to(dt, [np.inf, -np.inf, 0.0])
+        assert r[0] == np.inf and r[1] == -np.inf and r[2] == 0.0
+        assert np.isnan(oracle.round_to(dt, [np.nan])[0])
+        assert math.copysign(1.0, oracle.round_to(dt, [-0.0])[0]) < 0
+
+
+# --------------------------------------------------------------------------
+# P13: whole recurrence against the dense form, in float64.
+#   S_t = alpha_t S_{t-1} (I - beta_t k^ k^T) + beta_t v k^T,  o_t = S_t q^,
+# with the gate written in its closed form alpha = (1 + e^x)^(-e^A_log),
+# which equals exp(-exp(A_log) softplus(x)) (#46090 gate arguments).
+# --------------------------------------------------------------------------
+def dense_sequence(bt, pool64, bidx):
+    K, V, HK, HV = bt.K, bt.V, bt.HK, bt.HV
+    cu = bt.cu_seqlens.numpy()
+    start, L = int(cu[bidx]), int(cu[bidx + 1] - cu[bidx])
+    acc = int(bt.num_accepted_tokens[bidx])
+    si = bt.spec_state_indices.numpy()
+    r = int(si[bidx, max(acc - 1, 0)])
+    q = bt.q.double().numpy(); k = bt.k.double().numpy()
+    v = bt.v.double().numpy(); z = bt.z.double().numpy()
+    a = bt.a.double().numpy(); b = bt.b.double().numpy()
+    A = bt.A_log.double().numpy(); dtb = bt.dt_bias.double().numpy()
+    w = bt.norm_weight.double().numpy()
+    tix = None if bt.spec_token_indx is None else bt.spec_token_indx.numpy()
+    slots, outs = {}, {}
+    for h in range(HV):
+        kh = h // (HV // HK)
+        S = pool64[r, h].copy()
+        for t in range(L):
+            row = int(tix[start + t]) if tix is not None else start + t
+            x = a[row, h] + dtb[h]
+            alpha = (1.0 + np.exp(x)) ** (-np.exp(A[h]))
+            beta = 1.0 / (1.0 + np.exp(-b[row, h]))
+            kk = k[row, kh] / np.sqrt(k[row, kh] @ k[row, kh] + 1e-6)
+            qq = bt.scale * q[row, kh] / np.sqrt(q[row, kh] @ q[row, kh] + 1e-6)
+            S = alpha * S @ (np.eye(K) - beta * np.outer(kk, kk)) + beta * np.outer(v[row, h], kk)
+            o = S @ qq
+            y = o / np.sqrt(np.mean(o * o) + bt.norm_eps) * w * silu(z[row, h])
+            slots[(int(si[bidx, t]), h)] = S.copy()
+            outs[(row, h)] = y
+    return slots, outs
+
+
+@pytest.mark.parametrize("K,V,HK,HV,B,T", [(4, 4, 1, 2, 2, 3), (8, 8, 2, 4, 3, 4),
+                                           (8, 4, 1, 2, 2, 2), (128, 128, 1, 2, 1, 3)])
+@pytest.mark.parametrize("seed", [0, 1])
+def test_p13_dense_form(K, V, HK, HV, B, T, seed):
+    bt = with_pool_dtype(tiny(K=K, V=V, HK=HK, HV=HV, B=B, T=T, seed=seed), F64)
+    bt.q, bt.k, bt.v, bt.z = (x.double() for x in (bt.q, bt.k, bt.v, bt.z))
+    pool, out = orc_spec(bt, out_dtype=F64)
+    p0 = bt.pool.numpy()
+    for bi in range(B):
+        slots, outs = dense_sequence(bt, p0, bi)
+        for (s, h), S in slots.items():
+            np.testing.assert_allclose(pool[s, h].numpy(), S, rtol=1e-11, atol=1e-13)
+        for (row, h), y in outs.items():
+            np.testing.assert_allclose(out[row, h].numpy(), y, rtol=1e-10, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# Slot semantics (#46090 spec kernel: clamp, skip, per-token store;
+# #51674 item 1: rewind to the last accepted slot, store every token).
+# --------------------------------------------------------------------------
+def test_p1_touched_set_bruteforce():
+    base = workloads.make("C1")
+    T = base.T
+    for L, acc in itertools.product(range(T + 1), range(T + 1)):
+        bt = workloads.make("C1")
+        cu = [0, L, L + T]
+        bt.q, bt.k, bt.v, bt.z, bt.a, bt.b = (x[: L + T] for x in
+                                              (base.q, base.k, base.v, base.z, base.a, base.b))
+        bt.cu_seqlens = torch.tensor(cu, dtype=torch.int32)
+        bt.num_accepted_tokens = torch.tensor([acc, int(base.num_accepted_tokens[1])],
+                                              dtype=torch.int32)
+        pool, out = orc_spec(bt)
+        want = sorted(set(bt.spec_state_indices[0, :L].tolist()) |
+                      set(bt.spec_state_indices[1, :T].tolist()))
+        assert slots_touched(bt.pool, pool) == want
+        untouched = [s for s in range(bt.pool.shape[0]) if s not in want]
+        assert bitwise_equal(pool[untouched], bt.pool[untouched])
+        # every processed output row is written, and only those
+        assert (out.abs().sum(dim=(1, 2)) > 0).sum().item() == L + T
+
+
+def test_p2_clamp_acc0_equals_acc1():
+    bt0 = workloads.make("C1")
+    bt0.num_accepted_tokens = torch.tensor([0, 0], dtype=torch.int32)
+    bt1 = workloads.make("C1")
+    bt1.num_accepted_tokens = torch.tensor([1, 1], dtype=torch.int32)
+    p0, o0 = orc_spec(bt0)
+    p1, o1 = orc_spec(bt1)
+    assert bitwise_equal(p0, p1) and bitwise_equal(o0, o1)
+    # and acc=2 reads a different slot, so the clamp is what makes them equal
+    bt2 = workloads.make("C1")
+    bt2.num_accepted_tokens = torch.tensor([2, 2], dtype=torch.int32)
+    p2, _ = orc_spec(bt2)
+    assert not bitwise_equal(p0, p2)
+
+
+def test_p3_empty_sequence_skipped():
+    bt = tiny(B=3, T=3, q_lens=[2, 0, 3], seed=4)
+    out0 = torch.full((bt.n_tok, bt.HV, bt.V), 7.0)
+    pool, out = orc_spec(bt, out=out0.clone())
+    assert slots_touched(bt.pool, pool) == sorted(
+        bt.spec_state_indices[0, :2].tolist() + bt.spec_state_indices[2, :3].tolist())
+    # all rows belong to sequences 0 and 2; nothing left at 7
+    assert not (out == 7.0).any()
+    bt_all0 = tiny(B=2, T=3, q_lens=[0, 0], seed=4)
+    pool, out = orc_spec(bt_all0, out=torch.zeros((0, bt_all0.HV, bt_all0.V)))
+    assert bitwise_equal(pool, bt_all0.pool)
+
+
+def prefix_batch(full, lens):
+    """Copy of ``full`` where sequence i keeps only its first lens[i] rows."""
+    bt = copy.copy(full)
+    cu = full.cu_seqlens.tolist()
+    rows = sum((list(range(cu[i], cu[i] + n)) for i, n in enumerate(lens)), [])
+    bt.q, bt.k, bt.v, bt.z, bt.a, bt.b = (x[rows] for x in
+                                          (full.q, full.k, full.v, full.z, full.a, full.b))
+    bt.cu_seqlens = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32)
+    return bt
+
+
+@pytest.mark.parametrize("dt", DTYPES)
+def test_p4_prefix_property(dt):
+    """After a T-token run, slot spec_idx[b, j-1] equals the final slot of a
+    j-token run, for every j (each post-token state goes to its own slot)."""
+    full = with_pool_dtype(tiny(B=2, T=4, K=8, V=8, seed=5, acc_lo=1), dt)
+    pf, of = orc_spec(full)
+    for j in range(1, 5):
+        p, o = orc_spec(prefix_batch(full, [j, 4]))
+        s = int(full.spec_state_indices[0, j - 1])
+        assert bitwise_equal(p[s], pf[s])
+        assert bitwise_equal(o[:j], of[:j])
+
+
+@pytest.mark.parametrize("dt", DTYPES)
+def test_p5_rewind_equivalence(dt):
+    """Step 1 over T tokens then step 2 with acc=j equals step 1 over only the
+    j accepted tokens then step 2: the rewind reads exactly the state after
+    the accepted prefix (acc=0 behaves as acc=1)."""
+    T = 4
+    s1 = with_pool_dtype(tiny(B=2, T=T, K=8, V=8, seed=6, acc_lo=1), dt)
+    s2 = tiny(B=2, T=T, K=8, V=8, seed=7)   # the next step's tokens
+    s2.spec_state_indices = s1.spec_state_indices
+    pool1, _ = orc_spec(s1)
+    for j in range(0, T + 1):
+        s2.num_accepted_tokens = torch.tensor([j, j], dtype=torch.int32)
+        pa, oa = orc_spec(s2, pool=pool1)
+        jj = max(j, 1)
+        pool1s, _ = orc_spec(prefix_batch(s1, [jj, jj]))
+        pb, ob = orc_spec(s2, pool=pool1s)
+        assert bitwise_equal(oa, ob)
+        for bi in range(2):
+            for s in s2.spec_state_indices[bi].tolist():
+                assert bitwise_equal(pa[s], pb[s])
+
+
+def test_p6_all_accepted_equals_unrolled_decode():
+    T = 4
+    for dt, exact in ((F64, True), (torch.float32, False), (torch.bfloat16, False)):
+        bt = with_pool_dtype(tiny(B=1, T=T, K=8, V=8, HK=1, HV=2, seed=8,
+                                  acc_lo=1, acc_hi=1), dt)
+        bt.v = bt.v.double(); bt.z = bt.z.double()
+        ps, os_ = orc_spec(bt, out_dtype=F64)
+        r = int(bt.spec_state_indices[0, 0])
+        pool, out = bt.pool.clone(), torch.zeros((T, bt.HV, bt.V), dtype=F64)
+        for t in range(T):
+            pool, out = orc_decode(bt, torch.tensor([r], dtype=torch.int32),
+                                   token_indx=torch.tensor([t], dtype=torch.int32),
+                                   pool=pool, out=out, out_dtype=F64)
+        final = int(bt.spec_state_indices[0, T - 1])
+        if exact:
+            assert bitwise_equal(pool[r], ps[final])
+            assert bitwise_equal(out, os_)
+        else:
+            tol = 1e-6 if dt == torch.float32 else 3e-2
+            np.testing.assert_allclose(pool[r].double().numpy(), ps[final].double().numpy(),
+                                       rtol=tol, atol=tol)
+            assert rel_l2(out.numpy(), os_.numpy()) < (1e-5 if dt == torch.float32 else 3e-2)
+
+
+# --------------------------------------------------------------------------
+# Special cases of the gates and the delta rule.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16, torch.float16])
+def test_p7_identity_step(dt):
+    """A_log=-inf gives alpha=1 exactly, b=-inf gives beta=0 exactly: every
+    written slot equals the read slot byte for byte, and out is the gated
+    RMSNorm of S_0 q^."""
+    bt = with_pool_dtype(tiny(B=2, T=3, K=8, V=8, seed=9, acc_lo=1), dt)
+    bt.A_log = torch.full_like(bt.A_log, -math.inf)
+    bt.b = torch.full_like(bt.b, -math.inf)
+    pool, out = orc_spec(bt, out_dtype=F64)
+    for bi in range(2):
+        r = int(bt.spec_state_indices[bi, int(bt.num_accepted_tokens[bi]) - 1])
+        for t in range(3):
+            assert bitwise_equal(pool[int(bt.spec_state_indices[bi, t])], bt.pool[r])
+            row = 3 * bi + t
+            for h in range(bt.HV):
+                qv = bt.q[row, h // (bt.HV // bt.HK)].double().numpy()
+                qh = bt.scale * qv / np.sqrt(qv @ qv + 1e-6)
+                o = bt.pool[r, h].double().numpy() @ qh
+                y = o / np.sqrt(np.mean(o * o) + 1e-5) * bt.norm_weight.double().numpy() \
+                    * silu(bt.z[row, h].double().numpy())
+                np.testing.assert_allclose(out[row, h].numpy(), y, rtol=1e-12, atol=1e-15)
+
+
+def test_p8_pure_decay_closed_form():
+    """beta=0 and A_log = log(c), a + dt_bias = 0: alpha = 2^-c exactly in
+    exact arithmetic (softplus(0) = log 2), so S_t = 2^(-c t) S_0 and
+    o_t = S_t q^_t (read after the token's decay)."""
+    for c in (1.0, 2.0):
+        bt = with_pool_dtype(tiny(B=1, T=4, K=8, V=8, seed=10, acc_lo=1, acc_hi=1), F64)
+        bt.b = torch.full_like(bt.b, -math.inf)
+        bt.A_log = torch.full(bt.A_log.shape, math.log(c), dtype=F64)
+        bt.a = torch.zeros_like(bt.a)
+        bt.dt_bias = torch.zeros_like(bt.dt_bias)
+        bt.norm_eps = 1.0
+        pool, out = orc_spec(bt, out_dtype=F64)
+        r = int(bt.spec_state_indices[0, 0])
+        S0 = bt.pool[r].numpy()
+        for t in range(4):
+            St = pool[int(bt.spec_state_indices[0, t])].numpy()
+            np.testing.assert_allclose(St, S0 * 2.0 ** (-c * (t + 1)), rtol=1e-14)
+            o = recover_o(out[t].numpy(), bt.norm_weight.double().numpy(),
+                          bt.z[t].double().numpy(), 1.0)
+            for h in range(bt.HV):
+                qv = bt.q[t, 0].double().numpy()
+                qh = bt.scale * qv / np.sqrt(qv @ qv + 1e-6)
+                np.testing.assert_allclose(o[h], St[h] @ qh, rtol=1e-9, atol=1e-14)
+
+
+def test_p9_beta1_retrieves_v_any_alpha():
+    """beta=1 (b=+inf): S_t k^_t = v_t up to the L2-norm epsilon, whatever the
+    decay -- holds only if the decay is applied before the delta."""
+    bt = with_pool_dtype(tiny(B=2, T=4, K=8, V=8, seed=11), F64)
+    bt.b = torch.full_like(bt.b, math.inf)
+    bt.A_log = torch.full_like(bt.A_log, 0.5)   # alpha well below 1
+    pool, _ = orc_spec(bt, out_dtype=F64)
+    for bi in range(2):
+        for t in range(4):
+            row = 4 * bi + t
+            S = pool[int(bt.spec_state_indices[bi, t])].numpy()
+            kv = bt.k[row, 0].double().numpy()
+            kh = kv / np.sqrt(kv @ kv + 1e-6)
+            for h in range(bt.HV):
+                np.testing.assert_allclose(S[h] @ kh, bt.v[row, h].double().numpy(),
+                                           rtol=0, atol=1e-5)
+
+
+def test_p10_orthogonal_keys_replace_columns():
+    """alpha=1, beta=1 and k_t = c e_{i_t} (distinct i_t): each token replaces
+    column i_t by v_t (up to the norm epsilon); the other columns stay exact."""
+    T, K = 3, 8
+    bt = with_pool_dtype(tiny(B=1, T=T, K=K, V=K, seed=12, acc_lo=1, acc_hi=1), F64)
+    bt.A_log = torch.full_like(bt.A_log, -math.inf)
+    bt.b = torch.full_like(bt.b, math.inf)
+    cols = [5, 1, 6]
+    kk = torch.zeros_like(bt.k)
+    for t, i in enumerate(cols):
+        kk[t, 0, i] = 1000.0
+    bt.k = kk
+    pool, _ = orc_spec(bt, out_dtype=F64)
+    S = bt.pool[int(bt.spec_state_indices[0, 0])].numpy().copy()
+    for t, i in enumerate(cols):
+        S[:, :, i] = bt.v[t].double().numpy()
+        got = pool[int(bt.spec_state_indices[0, t])].numpy()
+        np.testing.assert_allclose(got, S, rtol=1e-11, atol=1e-11)
+        keep = [c for c in range(K) if c not in cols[: t + 1]]
+        assert np.array_equal(got[:, :, keep], bt.pool[int(bt.spec_state_indices[0, 0])]
+                              .numpy()[:, :, keep])
+
+
+def test_p11_l2norm_invariants():
+    """S_0 = 0, alpha = beta = 1: S_1 = v k^T exposes k^; its squared norm is
+    nk/(nk + 1e-6), and scaling k by c > 0 changes nothing but the eps effect."""
+    bt = with_pool_dtype(tiny(B=1, T=1, K=8, V=8, seed=13, acc_lo=1, acc_hi=1), F64)
+    bt.pool.zero_()
+    bt.A_log = torch.full_like(bt.A_log, -math.inf)
+    bt.b = torch.full_like(bt.b, math.inf)
+    pool, _ = orc_spec(bt, out_dtype=F64)
+    s = int(bt.spec_state_indices[0, 0])
+    kv = bt.k[0, 0].double().numpy()
+    nk = kv @ kv
+    for h in range(bt.HV):
+        S = pool[s, h].numpy()
+        vv = bt.v[0, h].double().numpy()
+        khat = S[0] / vv[0]
+        np.testing.assert_allclose(khat @ khat, nk / (nk + 1e-6), rtol=1e-13)
+        np.testing.assert_allclose(np.outer(vv, khat), S, rtol=1e-13, atol=1e-15)
+        assert np.all(np.sign(khat) == np.sign(kv))
+    for c in (0.25, 3.0):
+        bt2 = with_pool_dtype(tiny(B=1, T=1, K=8, V=8, seed=13, acc_lo=1, acc_hi=1), F64)
+        bt2.pool.zero_(); bt2.A_log = bt.A_log; bt2.b = bt.b
+        bt2.k = bt.k * c
+        p2, _ = orc_spec(bt2, out_dtype=F64)
+        np.testing.assert_allclose(p2[s].numpy(), pool[s].numpy(), rtol=1e-6)
+
+
+def test_p12_linearity():
+    """Scaling S_0 and every v by 2 doubles every stored state exactly and
+    every raw read-out o; by 3 to rounding."""
+    for c, exact in ((2.0, True), (3.0, False)):
+        bt = with_pool_dtype(tiny(B=2, T=3, K=8, V=8, seed=14, acc_lo=1), F64)
+        bt.v = bt.v.double(); bt.norm_eps = 1.0
+        p1, o1 = orc_spec(bt, out_dtype=F64)
+        bt2 = with_pool_dtype(tiny(B=2, T=3, K=8, V=8, seed=14, acc_lo=1), F64)
+        bt2.v = bt.v * c; bt2.pool = bt.pool * c; bt2.norm_eps = 1.0
+        p2, o2 = orc_spec(bt2, out_dtype=F64)
+        if exact:
+            assert bitwise_equal(p2, p1 * c)
+        else:
+            np.testing.assert_allclose(p2.numpy(), p1.numpy() * c, rtol=1e-12, atol=1e-15)
+        w, z = bt.norm_weight.double().numpy(), bt.z.double().numpy()
+        r1 = recover_o(o1.numpy(), w, z, 1.0)
+        r2 = recover_o(o2.numpy(), w, z, 1.0)
+        np.testing.assert_allclose(r2, c * r1, rtol=1e-8, atol=1e-12)
+
+
+def test_p14_gated_rmsnorm_closed_forms():
+    bt = with_pool_dtype(tiny(B=2, T=2, K=8, V=8, HV=3, seed=15), F64)
+    bt.norm_weight = torch.ones_like(bt.norm_weight)
+    # z = 0 -> y = 0 exactly
+    bt0 = with_pool_dtype(tiny(B=2, T=2, K=8, V=8, HV=3, seed=15), F64)
+    bt0.z = torch.zeros_like(bt0.z)
+    _, out0 = orc_spec(bt0, out=torch.full((4, 3, 8), 5.0, dtype=F64), out_dtype=F64)
+    assert (out0 == 0).all()
+    # per (token, v-head) over V: mean((y / silu z)^2) = ms / (ms + eps),
+    # where ms is the mean square of o = S_t q^ from the dense form
+    p0 = bt.pool.numpy()
+    for eps in (1e-5, 0.3):
+        bt.norm_eps = eps
+        _, out = orc_spec(bt, out_dtype=F64)
+        for bi in range(2):
+            slots, _ = dense_sequence(bt, p0, bi)
+            for t in range(2):
+                row = 2 * bi + t
+                S = {h: slots[(int(bt.spec_state_indices[bi, t]), h)] for h in range(3)}
+                kq = bt.q[row, 0].double().numpy()
+                qh = bt.scale * kq / np.sqrt(kq @ kq + 1e-6)
+                for h in range(3):
+                    o = S[h] @ qh
+                    ms = np.mean(o * o)
+                    u = out[row, h].numpy() / silu(bt.z[row, h].double().numpy())
+                    np.testing.assert_allclose(np.mean(u * u), ms / (ms + eps), rtol=1e-10)
+
+
+def test_p15_gqa_mapping_repeat_interleave():
+    """HK < HV equals HK' = HV with each key head copied to its G consecutive
+    v-heads (non-interleaved GQA, #46090 kh = ni / group_size)."""
+    bt = tiny(B=2, T=3, K=8, V=8, HK=2, HV=6, seed=16)
+    p, o = orc_spec(bt)
+    bt_r = tiny(B=2, T=3, K=8, V=8, HK=2, HV=6, seed=16)
+    bt_r.q = bt.q.repeat_interleave(3, dim=1)
+    bt_r.k = bt.k.repeat_interleave(3, dim=1)
+    pr, or_ = oracle.spec_update(bt_r.q, bt_r.k, bt.v, bt.z, bt.a, bt.b, bt.A_log,
+                                 bt.dt_bias, bt.norm_weight, bt.pool, bt.cu_seqlens,
+                                 bt.spec_state_indices, bt.num_accepted_tokens,
+                                 out_dtype=bt.out_dtype, scale=bt.scale)
+    assert bitwise_equal(p, pr) and bitwise_equal(o, or_)
+    qt, kt = bt.q.repeat(1, 3, 1), bt.k.repeat(1, 3, 1)   # tiled: wrong map
+    pt, _ = oracle.spec_update(qt, kt, bt.v, bt.z, bt.a, bt.b, bt.A_log, bt.dt_bias,
+                               bt.norm_weight, bt.pool, bt.cu_seqlens,
+                               bt.spec_state_indices, bt.num_accepted_tokens,
+                               out_dtype=bt.out_dtype, scale=bt.scale)
+    assert not bitwise_equal(p, pt)
+
+
+def test_p16_batch_independence_and_permutation():
+    bt = tiny(B=4, T=3, K=8, V=8, HV=2, seed=17, q_lens=[3, 1, 2, 3])
+    p, o = orc_spec(bt)
+    cu = bt.cu_seqlens.tolist()
+    # each sequence alone
+    for bi in range(4):
+        rows = list(range(cu[bi], cu[bi + 1]))
+        p1, o1 = oracle.spec_update(
+            bt.q[rows], bt.k[rows], bt.v[rows], bt.z[rows], bt.a[rows], bt.b[rows],
+            bt.A_log, bt.dt_bias, bt.norm_weight, bt.pool,
+            torch.tensor([0, len(rows)], dtype=torch.int32),
+            bt.spec_state_indices[bi: bi + 1], bt.num_accepted_tokens[bi: bi + 1],
+            out_dtype=bt.out_dtype, scale=bt.scale)
+        assert bitwise_equal(o1, o[rows])
+        for s in bt.spec_state_indices[bi, : len(rows)].tolist():
+            assert bitwise_equal(p1[s], p[s])
+    # sequences permuted
+    perm = [2, 0, 3, 1]
+    rows = sum((list(range(cu[i], cu[i + 1])) for i in perm), [])
+    lens = [cu[i + 1] - cu[i] for i in perm]
+    cup = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32)
+    pp, op = oracle.spec_update(
+        bt.q[rows], bt.k[rows], bt.v[rows], bt.z[rows], bt.a[rows], bt.b[rows],
+        bt.A_log, bt.dt_bias, bt.norm_weight, bt.pool, cup,
+        bt.spec_state_indices[perm], bt.num_accepted_tokens[perm],
+        out_dtype=bt.out_dtype, scale=bt.scale)
+    assert bitwise_equal(pp, p) and bitwise_equal(op, o[rows])
+
+
+def test_p17_gather_alignment():
+    """#51812: one gather index must select q/k/v/z *and* a/b.  A run with a
+    non-identity token_indx equals the run on pre-gathered tensors; feeding
+    ungathered gates (the bug the report fixes) differs."""
+    mb = workloads.mixed_batch(n_non_spec=3, n_spec=3, T=3, HK=1, HV=2, K=8, V=8,
+                               act="f32", state="f32", seed=18)
+    ti = mb.spec_token_indx
+    assert not torch.equal(ti, torch.arange(ti.numel(), dtype=torch.int32))
+    p, o = orc_spec(mb)
+    g = ti.long()
+    pg, og = oracle.spec_update(mb.q[g], mb.k[g], mb.v[g], mb.z[g], mb.a[g], mb.b[g],
+                                mb.A_log, mb.dt_bias, mb.norm_weight, mb.pool,
+                                mb.cu_seqlens, mb.spec_state_indices,
+                                mb.num_accepted_tokens, out_dtype=mb.out_dtype,
+                                scale=mb.scale)
+    assert bitwise_equal(pg, p) and bitwise_equal(og, o[g])
+    untouched = [r for r in range(mb.n_tok) if r not in ti.tolist()]
+    assert (o[untouched] == 0).all()
+    n = ti.numel()
+    pb, _ = oracle.spec_update(mb.q[g], mb.k[g], mb.v[g], mb.z[g], mb.a[:n], mb.b[:n],
+                               mb.A_log, mb.dt_bias, mb.norm_weight, mb.pool,
+                               mb.cu_seqlens, mb.spec_state_indices,
+                               mb.num_accepted_tokens, out_dtype=mb.out_dtype,
+                               scale=mb.scale)
+    assert not bitwise_equal(pb, p)
+
+
+def test_p18_mixed_batch_equals_per_unit():
+    mb = workloads.mixed_batch(n_non_spec=4, n_spec=3, T=3, HK=1, HV=2, K=8, V=8,
+                               act="f32", state="bf16", seed=19)
+    p, o = orc_spec(mb)
+    p, o = orc_decode(mb, mb.state_indices, token_indx=mb.non_spec_token_indx,
+                      pool=p, out=o)
+    spec_rows = set(mb.spec_token_indx.tolist())
+    ns_rows = set(mb.non_spec_token_indx.tolist())
+    assert spec_rows.isdisjoint(ns_rows) and spec_rows | ns_rows == set(range(mb.n_tok))
+    spec_slots = set(mb.spec_state_indices.flatten().tolist())
+    assert spec_slots.isdisjoint(set(mb.state_indices.tolist()))
+    # every unit on its own
+    for i, (s, row) in enumerate(zip(mb.state_indices.tolist(),
+                                     mb.non_spec_token_indx.tolist())):
+        p1, o1 = orc_decode(mb, torch.tensor([s], dtype=torch.int32),
+                            token_indx=torch.tensor([row], dtype=torch.int32))
+        assert bitwise_equal(p1[s], p[s]) and bitwise_equal(o1[row], o[row])
+    T = mb.T
+    for bi in range(mb.num_seqs):
+        rows = mb.spec_token_indx[bi * T:(bi + 1) * T]
+        p1, o1 = oracle.spec_update(
+            mb.q, mb.k, mb.v, mb.z, mb.a, mb.b, mb.A_log, mb.dt_bias,
+            mb.norm_weight, mb.pool, torch.tensor([0, T], dtype=torch.int32),
+            mb.spec_state_indices[bi: bi + 1], mb.num_accepted_tokens[bi: bi + 1],
+            token_indx=rows, out_dtype=mb.out_dtype, scale=mb.scale)
+        for s in mb.spec_state_indices[bi].tolist():
+            assert bitwise_equal(p1[s], p[s])
+        assert bitwise_equal(o1[rows.long()], o[rows.long()])
+
+
+# --------------------------------------------------------------------------
+# Non-spec entry: negative slots are padding; indices are validated.
+# --------------------------------------------------------------------------
+def test_decode_negative_slot_is_padding():
+    bt = tiny(B=1, T=3, K=8, V=8, seed=20)
+    si = torch.tensor([int(bt.spec_state_indices[0, 0]), -1, int(bt.spec_state_indices[0, 2])],
+                      dtype=torch.int32)
+    out0 = torch.full((3, bt.HV, bt.V), 9.0)
+    p, o = orc_decode(bt, si, out=out0)
+    assert slots_touched(bt.pool, p) == sorted([int(si[0]), int(si[2])])
+    assert (o[1] == 9.0).all() and not (o[0] == 9.0).any()
+
+
+def test_oracle_rejects_bad_indices():
+    bt = tiny(B=2, T=3, seed=21)
+    bad = bt.spec_state_indices.clone()
+    bad[1, 2] = bt.pool.shape[0]
+    with pytest.raises(ValueError):
+        orc_spec(bt, spec_state_indices=bad)
+    with pytest.raises(ValueError):
+        orc_spec(bt, num_accepted_tokens=torch.tensor([4, 0], dtype=torch.int32))
+    with pytest.raises(ValueError):
+        orc_decode(bt, torch.tensor([0, 99, 1], dtype=torch.int32))
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16, torch.float16])
+def test_store_rounding_points(dt):
+    """#52191 item 4: arithmetic stays wide and only the slot store goes
+    through the state type.  So every stored post-token state equals the
+    nearest-even rounding of the same run carried with no rounding at all
+    (float64 storage), token after token -- which fails if the carry itself
+    were rounded between tokens or if the wrong format were used.  The same
+    holds for the output rows."""
+    bt = with_pool_dtype(tiny(B=2, T=4, K=8, V=8, seed=22, acc_lo=1), dt)
+    p_dt, o_dt = orc_spec(bt, out_dtype=dt)
+    wide = copy.copy(bt)
+    wide.pool = bt.pool.to(F64)
+    p64, o64 = orc_spec(wide, out_dtype=F64)
+    for s in bt.spec_state_indices.flatten().tolist():
+        want = oracle.round_to(dt, p64[s].numpy())
+        assert np.array_equal(p_dt[s].to(F64).numpy(), want)
+    assert np.array_equal(o_dt.to(F64).numpy(), oracle.round_to(dt, o64.numpy()))
