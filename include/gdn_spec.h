@@ -1,0 +1,205 @@
+/*
+ * gdn_spec.h -- C ABI of the MI355X (gfx950) fused Gated DeltaNet (GDN)
+ * speculative-decode state update.
+ *
+ * The operation is the fused post-conv MTP decode step described by the vLLM
+ * PR reports on prhub.com.cn:
+ *   #51674 "[Kernel][Perf] Add fused CUDA post-conv MTP decode kernel for
+ *          Qwen3.5 GDN", 实现拆解 (implementation breakdown) item 1: per
+ *          (request, value head) rewind to the last accepted state slot, run
+ *          the gated delta-rule recurrence over up to 8 draft tokens, store
+ *          every post-token state, finish with a gated RMSNorm; item 2 and the
+ *          vllm/_custom_ops.py excerpt: the argument list and the defaults
+ *          scale = 128**-0.5, norm_eps = 1e-5.
+ *   #46090 "[CPU][Spec Decode] Support DFlash speculative decoding for GDN
+ *          models on CPU", 关键源码片段 (key source excerpts), fla.cpp: the
+ *          variable-length batch (cu_seqlens, q_len <= 0 skipped), the clamp
+ *          max(num_accepted - 1, 0), per-token slots spec_state_indices[b, t],
+ *          per-tensor token/head strides, non-interleaved GQA.
+ *   #52191 "[CPU] Support FP16/BF16 persisted GDN state on AMX", 实现拆解
+ *          item 4: arithmetic in FP32, only slot reads and writes in the state
+ *          dtype (fp32, bf16 or fp16).
+ *   #51812 "[Bugfix] Align Qwen GDN gates with speculative tokens",
+ *          关键源码片段: the same token index gathers q/k/v and the gates a/b.
+ *
+ * Per (sequence b, value head h) with L = cu_seqlens[b+1] - cu_seqlens[b] > 0:
+ *   r     = spec_state_indices[b][max(num_accepted_tokens[b] - 1, 0)]
+ *   S     = float(pool[r][h])                       (V x K, read once)
+ *   for t < L, row = token_indx ? token_indx[cu[b]+t] : cu[b]+t:
+ *     alpha = exp(-exp(A_log[h]) * softplus(a[row][h] + dt_bias[h]))
+ *     beta  = sigmoid(b[row][h])
+ *     k^ = k[row][kh] / sqrt(|k|^2 + 1e-6),  q^ = scale * q[row][kh] / sqrt(|q|^2 + 1e-6)
+ *     S  = alpha S;  S += beta (v[row][h] - S k^) k^T;  o = S q^
+ *     pool[spec_state_indices[b][t]][h] = round_to_state_dtype(S)
+ *     out[row][h] = o / sqrt(mean(o^2) + norm_eps) * norm_weight * silu(z[row][h])
+ *   with kh = h / (HV / HK).  The FP32 carry S is not re-rounded between
+ *   tokens; rounding happens only at the slot and output stores (to nearest,
+ *   ties to even).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers, owned by the caller.  The
+ *     library allocates nothing, keeps no state between calls and never
+ *     synchronises: the call enqueues one kernel on `stream` and returns.
+ *     Launches are therefore capturable in a HIP graph.  Faults surface at
+ *     the caller's next synchronisation.
+ *   - Strides are in elements.  The innermost (head-dim) stride is 1.
+ *   - Only the rows of processed tokens are written in `out`; other rows keep
+ *     their contents (callers that pad batches zero-initialise `out`).
+ *   - Only the slots spec_state_indices[b][t] (t < L_b), resp.
+ *     state_indices[i] >= 0, change; every other byte of the pool is kept.
+ *   - Host-checkable argument errors return GDN_ERR_INVALID, unsupported
+ *     shapes or dtypes GDN_ERR_UNSUPPORTED, a failed launch GDN_ERR_DEVICE;
+ *     each sets a thread-local reason returned by gdn_last_error().  Nothing
+ *     is enqueued on any error.  There is no fallback path.
+ *   - Device-side metadata is trusted, as on the pages, with one safety net:
+ *     a unit whose metadata is out of range (acc < 0 or > spec_stride,
+ *     L > 8 or > spec_stride, a slot outside [0, num_slots), a row outside
+ *     [0, n_tok)) is skipped whole -- nothing read or written for it.
+ *     Distinct write slots, and no read slot of one sequence equal to a write
+ *     slot of another, are the caller's contract (data races otherwise);
+ *     gdn_validate_indices_host() checks all of it on host copies.
+ */
+#ifndef GDN_SPEC_H
+#define GDN_SPEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+#define GDN_MAX_DRAFT_TOKENS 8
+#define GDN_HEAD_DIM 128
+
+typedef enum { GDN_F32 = 0, GDN_F16 = 1, GDN_BF16 = 2 } gdn_dtype;
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_INVALID = 1,
+    GDN_ERR_UNSUPPORTED = 2,
+    GDN_ERR_DEVICE = 3
+} gdn_status;
+
+/* A strided 3-D (or 2-D) device tensor [n_tok][heads][dim], dim contiguous.
+ * For the gates a and b ([n_tok][HV]) stride_head must be 1. */
+typedef struct {
+    void*   data;
+    int64_t stride_tok;
+    int64_t stride_head;
+} gdn_view;
+
+/* One layer's activations, parameters and output.
+ *   q, k : [n_tok][num_k_heads][head_k_dim]   act_dtype, read
+ *   v, z : [n_tok][num_v_heads][head_v_dim]   act_dtype, read (z = output gate)
+ *   a, b : [n_tok][num_v_heads]               act_dtype, read (gate inputs)
+ *   out  : [n_tok][num_v_heads][head_v_dim]   out_dtype, written
+ *   A_log, dt_bias : fp32 [num_v_heads];  norm_weight : fp32 [head_v_dim]
+ * A packed mixed_qkv projection is passed as three views into it.
+ * With n_tok == 0 the activation/output pointers may be NULL and every call
+ * is a no-op.
+ * Alignment: q, k, v, z, out data pointers aligned to 2 elements and their
+ * token/head strides even; A_log, dt_bias, norm_weight 4-byte aligned. */
+typedef struct {
+    gdn_view q, k, v, z, a, b, out;
+    const float* A_log;
+    const float* dt_bias;
+    const float* norm_weight;
+    int32_t act_dtype;    /* gdn_dtype */
+    int32_t out_dtype;    /* gdn_dtype */
+    int32_t num_k_heads;  /* HK */
+    int32_t num_v_heads;  /* HV, a multiple of HK */
+    int32_t head_k_dim;   /* K, must be 128 */
+    int32_t head_v_dim;   /* V, must be 128 */
+    int64_t n_tok;        /* rows addressable in q..out */
+    float   scale;        /* applied to the normalised q; K^-0.5 by default */
+    float   norm_eps;     /* RMSNorm epsilon; 1e-5 by default */
+} gdn_layer;
+
+/* The recurrent-state pool, contiguous [num_slots][num_v_heads][V][K]
+ * (K innermost), updated in place.  16-byte aligned. */
+typedef struct {
+    void*   data;
+    int32_t dtype;        /* gdn_dtype */
+    int32_t reserved;
+    int64_t num_slots;
+} gdn_state_pool;
+
+/*
+ * Speculative (MTP) update of num_seqs sequences, one workgroup per
+ * (sequence, value head).
+ *   cu_seqlens          int32 [num_seqs+1]  row offsets of each sequence in
+ *                                            the (gathered) token space
+ *   max_q_len           host bound on every L_b, 1..8
+ *   spec_state_indices  int32 [num_seqs][spec_stride]  slot of each draft
+ *                                            token's post-token state
+ *   num_accepted_tokens int32 [num_seqs]    accepted tokens of the previous
+ *                                            step; the state is read from slot
+ *                                            [b][max(acc - 1, 0)]
+ *   token_indx          int32 [cu_seqlens[num_seqs]] or NULL: row of q/k/v/z/
+ *                                            a/b/out used by gathered token i
+ *                                            (NULL: row = i)
+ * Reads the pool at the rewind slots, writes it at the draft-token slots,
+ * writes out at the processed rows.
+ */
+gdn_status gdn_spec_decode_update(const gdn_layer* layer,
+                                  const gdn_state_pool* pool,
+                                  const int32_t* cu_seqlens, int32_t num_seqs,
+                                  int32_t max_q_len,
+                                  const int32_t* spec_state_indices,
+                                  int32_t spec_stride,
+                                  const int32_t* num_accepted_tokens,
+                                  const int32_t* token_indx,
+                                  hipStream_t stream);
+
+/*
+ * Non-speculative decode: num_tokens single-token updates, entry i reading
+ * and writing slot state_indices[i] in place (a negative slot marks padding:
+ * skipped, its output row untouched).  token_indx int32 [num_tokens] or NULL
+ * gives the row of entry i (NULL: row = i).  Same recurrence with L = 1.
+ */
+gdn_status gdn_decode_update(const gdn_layer* layer, const gdn_state_pool* pool,
+                             const int32_t* state_indices, int32_t num_tokens,
+                             const int32_t* token_indx, hipStream_t stream);
+
+/*
+ * Host-side check of the metadata contract on HOST copies of the index
+ * arrays (any pointer may be NULL when its count is 0; the token-index arrays
+ * may be NULL for the identity).  Returns GDN_OK, or GDN_ERR_INVALID with the
+ * first violation in gdn_last_error(): cu_seqlens not non-decreasing from 0,
+ * L_b > max_q_len or > spec_stride, acc outside [0, spec_stride], a slot
+ * outside [0, num_slots), a row outside [0, n_tok), a write slot used twice,
+ * a read slot of one sequence written by another (or by a non-spec entry),
+ * a row used twice.  The spec entries and the non-spec entries of one mixed
+ * batch are checked together.
+ */
+gdn_status gdn_validate_indices_host(int64_t num_slots, int64_t n_tok,
+                                     const int32_t* cu_seqlens,
+                                     int32_t num_seqs, int32_t max_q_len,
+                                     const int32_t* spec_state_indices,
+                                     int32_t spec_stride,
+                                     const int32_t* num_accepted_tokens,
+                                     const int32_t* spec_token_indx,
+                                     const int32_t* state_indices,
+                                     int32_t num_non_spec,
+                                     const int32_t* non_spec_token_indx);
+
+/* Reason for the last non-OK status returned on this thread ("" if none). */
+const char* gdn_last_error(void);
+
+/* Static name of a status code. */
+const char* gdn_status_string(gdn_status status);
+
+/* GDN_ABI_VERSION of the built library, and the sizes of the argument
+ * structs it was built with, so bindings can check their layout. */
+int32_t gdn_abi_version(void);
+void gdn_abi_struct_sizes(size_t* view, size_t* layer, size_t* pool);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_SPEC_H */

@@ -1,0 +1,549 @@
+// gdn_kernels.hip -- fused Gated DeltaNet speculative-decode state update for
+// CDNA4 (gfx950), and the two C-ABI launch entry points.
+//
+// What is computed is fixed by the vLLM PR reports on prhub.com.cn (#51674
+// 实现拆解 item 1: one block per (request, value head), rewind by
+// num_accepted_tokens, serial recurrence over <= 8 draft tokens, every
+// post-token state stored to its slot, gated RMSNorm epilogue; #46090 fla.cpp
+// excerpt: clamp, skip, GQA map; #52191 实现拆解 item 4: FP32 arithmetic,
+// state-dtype slot stores; #51812: one gather index for q/k/v and a/b).
+//
+// How it is computed here (not the pages' CUDA design):
+//   * One 256-thread workgroup (4 wave64) per (sequence, value head); a 1-D
+//     grid of num_seqs*HV workgroups.
+//   * The 128x128 state tile (V rows, K contiguous) lives in registers for
+//     the whole draft: each 8-lane group owns one row at a time, each lane 16
+//     of its elements, and every lane holds 4 rows (64 fp32 values).  A row
+//     chunk moves as one 16-byte access per lane, so one wave instruction
+//     covers eight full 128-byte lines.  The tile is read from HBM once and
+//     written once per draft token; nothing else touches it.
+//   * Rows of S evolve independently.  Per token and row, the two dot
+//     products of the OLD row (S.k^ and S.q^) are reduced together over the
+//     8 lanes with three DPP steps; then
+//        d = beta (v - alpha S.k^),  o = alpha S.q^ + d (k^.q^),
+//        S = alpha S + d k^
+//     which is S_t q^ of the updated state without a second pass.
+//   * Per-token vectors (k^, q^, v) and scalars (alpha, beta, k^.q^) are
+//     computed once per workgroup in a prologue and shared through LDS; the
+//     read-outs o go to LDS for the per-(token, head) RMSNorm epilogue.
+//   * No MFMA: a rank-1 recurrence is not a dense contraction.  The kernel is
+//     bound by HBM bandwidth (8 of 9 tile transfers at T=8 are stores).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <type_traits>
+
+#include "gdn_internal.h"
+
+namespace {
+
+constexpr int D = GDN_HEAD_DIM;          // K = V = 128
+constexpr int MAXT = GDN_MAX_DRAFT_TOKENS;
+constexpr int NTHREADS = 256;
+constexpr int ROWS_PER_WAVE = D / (NTHREADS / 64);   // 32
+constexpr int RPT = ROWS_PER_WAVE / 8;               // rows per thread: 4
+constexpr int NE = D / 8;                            // elements per (thread, row): 16
+
+struct KParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* z;
+    const void* a;
+    const void* b;
+    void* out;
+    int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh, z_st, z_sh, a_st, b_st, o_st, o_sh;
+    const float* A_log;
+    const float* dt_bias;
+    const float* norm_weight;
+    void* pool;
+    int64_t num_slots;
+    int64_t n_tok;
+    int32_t HV;
+    int32_t group;        // HV / HK
+    float scale;
+    float norm_eps;
+    const int32_t* cu;
+    const int32_t* spec_idx;
+    const int32_t* num_acc;
+    const int32_t* tix;
+    const int32_t* state_idx;
+    int32_t spec_stride;
+};
+
+// ---- element conversions -------------------------------------------------
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Raw bits of two consecutive elements: one dword for 16-bit types, two for
+// fp32.  Loads keep raw bits so that conversion waits can be deferred.
+template <int DT>
+struct Pair {
+    using raw = typename std::conditional<DT == GDN_F32, uint2, uint32_t>::type;
+};
+
+template <int DT>
+__device__ __forceinline__ float2 unpack_pair(typename Pair<DT>::raw w)
+{
+    if constexpr (DT == GDN_F32) {
+        return make_float2(__uint_as_float(w.x), __uint_as_float(w.y));
+    } else if constexpr (DT == GDN_BF16) {
+        return make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+    } else {
+        const f16x2 h = __builtin_bit_cast(f16x2, w);
+        return make_float2(static_cast<float>(h.x), static_cast<float>(h.y));
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ float unpack_one(uint32_t w)
+{
+    if constexpr (DT == GDN_F32)
+        return __uint_as_float(w);
+    else if constexpr (DT == GDN_BF16)
+        return __uint_as_float(w << 16);
+    else
+        return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w)));
+}
+
+// Two values rounded to nearest even into one dword (low element first);
+// gfx950 converts the pair in one instruction.
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi)
+{
+    const f32x2 x = {lo, hi};
+    if constexpr (DT == GDN_BF16)
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+    else
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, f16x2));
+}
+
+template <int DT>
+__device__ __forceinline__ typename Pair<DT>::raw load_pair_raw(const void* base, int64_t idx)
+{
+    if constexpr (DT == GDN_F32)
+        return *reinterpret_cast<const uint2*>(static_cast<const float*>(base) + idx);
+    else
+        return *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(base) + idx);
+}
+
+template <int DT>
+__device__ __forceinline__ uint32_t load_one_raw(const void* base, int64_t idx)
+{
+    if constexpr (DT == GDN_F32)
+        return static_cast<const uint32_t*>(base)[idx];
+    else
+        return static_cast<const uint16_t*>(base)[idx];
+}
+
+template <int DT>
+__device__ __forceinline__ void store_pair(void* base, int64_t idx, float2 x)
+{
+    if constexpr (DT == GDN_F32)
+        *reinterpret_cast<float2*>(static_cast<float*>(base) + idx) = x;
+    else
+        *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(base) + idx) = pack2<DT>(x.x, x.y);
+}
+
+// ---- cross-lane sums -------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x)
+{
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over each aligned group of 8 lanes; every lane of the group gets the
+// same bits: quad_perm(1,0,3,2), quad_perm(2,3,0,1), row_half_mirror.
+__device__ __forceinline__ float sum8(float x)
+{
+    x += dpp<0xB1>(x);
+    x += dpp<0x4E>(x);
+    x += dpp<0x141>(x);
+    return x;
+}
+
+// Sum over the wave; wave-uniform result.
+__device__ __forceinline__ float sum64(float x)
+{
+    x = sum8(x);
+    x += dpp<0x140>(x);  // row_mirror: 16-lane sums
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
+// ---- the kernel ------------------------------------------------------------
+// ACT, ST, OUT: gdn_dtype of activations, state pool, output.  SPEC selects
+// the speculative metadata (cu_seqlens / spec_state_indices / num_accepted)
+// or the single-token in-place form (state_indices).
+template <int ACT, int ST, int OUT, bool SPEC>
+__global__ void __launch_bounds__(NTHREADS)
+gdn_update_kernel(const KParams p)
+{
+    constexpr int ESZ = (ST == GDN_F32) ? 4 : 2;   // state element bytes
+    constexpr int CH = D * ESZ / 128;              // 16-byte chunks per (thread,row): 4 or 2
+    constexpr int EPC = 16 / ESZ;                  // elements per chunk: 4 or 8
+    constexpr int CSTRIDE = D / CH;                // row offset between chunks: 32 or 64
+    constexpr int NT = SPEC ? MAXT : 1;            // static bound on draft tokens
+    static_assert(CH * EPC == NE, "layout");
+
+    // 16-byte aligned: the token loop reads k^ and q^ as float4.
+    __shared__ __attribute__((aligned(16))) float sK[NT][D];
+    __shared__ __attribute__((aligned(16))) float sQ[NT][D];
+    __shared__ __attribute__((aligned(16))) float sV[NT][D];
+    __shared__ __attribute__((aligned(16))) float sO[NT][D];
+    __shared__ float sAlpha[NT], sBeta[NT], sKQ[NT];
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int g = lane >> 3;   // row within the wave's 8-row band
+    const int j = lane & 7;    // position within the row's 8-lane group
+
+    const int64_t unit = blockIdx.x;
+    const int64_t seq = unit / p.HV;
+    const int h = static_cast<int>(unit - seq * p.HV);
+    const int kh = h / p.group;
+
+    // ---- unit metadata (uniform), fetched in one batch ----
+    int L;
+    int64_t c0, rslot;
+    int64_t wslot[NT];
+    if constexpr (SPEC) {
+        c0 = p.cu[seq];
+        L = static_cast<int>(p.cu[seq + 1] - c0);
+        const int acc = p.num_acc[seq];
+        if (L <= 0)
+            return;  // q_len <= 0: nothing read, written or output
+        if (L > MAXT || L > p.spec_stride || acc < 0 || acc > p.spec_stride)
+            return;
+        const int32_t* sidx = p.spec_idx + seq * p.spec_stride;
+        rslot = sidx[acc > 1 ? acc - 1 : 0];
+        bool bad = rslot < 0 || rslot >= p.num_slots;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int tt = t < L ? t : L - 1;
+            wslot[t] = sidx[tt];
+            const int64_t row = p.tix ? p.tix[c0 + tt] : c0 + tt;
+            bad |= wslot[t] < 0 || wslot[t] >= p.num_slots || row < 0 || row >= p.n_tok;
+        }
+        if (bad)
+            return;
+    } else {
+        rslot = p.state_idx[seq];
+        c0 = seq;
+        L = 1;
+        wslot[0] = rslot;
+        const int64_t row = p.tix ? p.tix[seq] : seq;
+        if (rslot < 0 || rslot >= p.num_slots || row < 0 || row >= p.n_tok)
+            return;
+    }
+
+    // ---- prologue loads: this wave's tokens t = wave, wave + 4 (clamped to
+    // the last token, so every lane loads a valid address and no branch
+    // forces an early wait) ----
+    constexpr int NTW = (NT + 3) / 4;   // tokens per wave
+    typename Pair<ACT>::raw qr[NTW], kr[NTW], vr[NTW], zr[NTW];
+    uint32_t ar[NTW], br[NTW];
+    int64_t rowv[NTW];
+#pragma unroll
+    for (int i = 0; i < NTW; ++i) {
+        const int t = wave + 4 * i;
+        const int tt = t < L ? t : L - 1;
+        const int64_t row = p.tix ? p.tix[c0 + tt] : c0 + tt;
+        rowv[i] = row;
+        qr[i] = load_pair_raw<ACT>(p.q, row * p.q_st + kh * p.q_sh + 2 * lane);
+        kr[i] = load_pair_raw<ACT>(p.k, row * p.k_st + kh * p.k_sh + 2 * lane);
+        vr[i] = load_pair_raw<ACT>(p.v, row * p.v_st + h * p.v_sh + 2 * lane);
+        zr[i] = load_pair_raw<ACT>(p.z, row * p.z_st + h * p.z_sh + 2 * lane);
+        ar[i] = load_one_raw<ACT>(p.a, row * p.a_st + h);
+        br[i] = load_one_raw<ACT>(p.b, row * p.b_st + h);
+    }
+    const float A = -expf(p.A_log[h]);
+    const float dtb = p.dt_bias[h];
+    const float2 wn = *reinterpret_cast<const float2*>(p.norm_weight + 2 * lane);
+
+    // ---- the rewind tile: read once, 16 B per lane per chunk ----
+    const size_t tile = static_cast<size_t>(D) * D;
+    const char* rbase = static_cast<const char*>(p.pool) +
+                        (static_cast<size_t>(rslot) * p.HV + h) * tile * ESZ;
+    uint4 raw[RPT][CH];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+        const int row = wave * ROWS_PER_WAVE + r * 8 + g;
+#pragma unroll
+        for (int c = 0; c < CH; ++c)
+            raw[r][c] = *reinterpret_cast<const uint4*>(
+                rbase + (static_cast<size_t>(row) * D + c * CSTRIDE + j * EPC) * ESZ);
+    }
+
+    // ---- prologue compute: gates, normalised k and q, k^.q^ ----
+    float2 zv[NTW];
+#pragma unroll
+    for (int i = 0; i < NTW; ++i) {
+        const int t = wave + 4 * i;
+        const float2 qv = unpack_pair<ACT>(qr[i]);
+        const float2 kv = unpack_pair<ACT>(kr[i]);
+        zv[i] = unpack_pair<ACT>(zr[i]);
+        const float nq = sum64(qv.x * qv.x + qv.y * qv.y);
+        const float nk = sum64(kv.x * kv.x + kv.y * kv.y);
+        const float rk = 1.0f / sqrtf(nk + 1e-6f);
+        const float rq = p.scale / sqrtf(nq + 1e-6f);
+        const float2 kn = make_float2(kv.x * rk, kv.y * rk);
+        const float2 qn = make_float2(qv.x * rq, qv.y * rq);
+        const float kq = sum64(kn.x * qn.x + kn.y * qn.y);
+        if (t < L) {
+            *reinterpret_cast<float2*>(&sK[t][2 * lane]) = kn;
+            *reinterpret_cast<float2*>(&sQ[t][2 * lane]) = qn;
+            *reinterpret_cast<float2*>(&sV[t][2 * lane]) = unpack_pair<ACT>(vr[i]);
+            if (lane == 0) {
+                const float x = unpack_one<ACT>(ar[i]) + dtb;
+                const float sp = x > 20.0f ? x : log1pf(expf(x));
+                sAlpha[t] = expf(A * sp);
+                sBeta[t] = 1.0f / (1.0f + expf(-unpack_one<ACT>(br[i])));
+                sKQ[t] = kq;
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- tile to fp32 registers ----
+    float S[RPT][NE];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const uint32_t w[4] = {raw[r][c].x, raw[r][c].y, raw[r][c].z, raw[r][c].w};
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                if constexpr (ST == GDN_F32) {
+                    S[r][c * 4 + m] = __uint_as_float(w[m]);
+                } else {
+                    const float2 f = unpack_pair<ST>(w[m]);
+                    S[r][c * 8 + 2 * m] = f.x;
+                    S[r][c * 8 + 2 * m + 1] = f.y;
+                }
+            }
+        }
+    }
+
+    // ---- the draft tokens, strictly in order (unrolled: the tile stays in
+    // the same registers from token to token) ----
+    char* pool = static_cast<char*>(p.pool);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        if (t >= L)
+            break;
+        // Keep the scheduler from hoisting the next token's LDS reads into
+        // this one: that only raises register pressure.
+        __builtin_amdgcn_sched_barrier(0);
+        const float alpha = sAlpha[t];
+        const float beta = sBeta[t];
+        const float kq = sKQ[t];
+        float kn[NE], qn[NE];
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+#pragma unroll
+            for (int m = 0; m < EPC; m += 4) {
+                const float4 k4 = *reinterpret_cast<const float4*>(&sK[t][c * CSTRIDE + j * EPC + m]);
+                const float4 q4 = *reinterpret_cast<const float4*>(&sQ[t][c * CSTRIDE + j * EPC + m]);
+                kn[c * EPC + m + 0] = k4.x; kn[c * EPC + m + 1] = k4.y;
+                kn[c * EPC + m + 2] = k4.z; kn[c * EPC + m + 3] = k4.w;
+                qn[c * EPC + m + 0] = q4.x; qn[c * EPC + m + 1] = q4.y;
+                qn[c * EPC + m + 2] = q4.z; qn[c * EPC + m + 3] = q4.w;
+            }
+        }
+        char* wbase = pool + (static_cast<size_t>(wslot[t]) * p.HV + h) * tile * ESZ;
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
+            const int row = wave * ROWS_PER_WAVE + r * 8 + g;
+            float pk = 0.0f, pq = 0.0f;
+#pragma unroll
+            for (int e = 0; e < NE; ++e) {
+                pk = fmaf(S[r][e], kn[e], pk);
+                pq = fmaf(S[r][e], qn[e], pq);
+            }
+            pk = sum8(pk);
+            pq = sum8(pq);
+            const float d = beta * (sV[t][row] - alpha * pk);
+            const float o = fmaf(alpha, pq, d * kq);
+#pragma unroll
+            for (int e = 0; e < NE; ++e)
+                S[r][e] = fmaf(d, kn[e], alpha * S[r][e]);
+            if (j == 0)
+                sO[t][row] = o;
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+                uint4 w;
+                if constexpr (ST == GDN_F32) {
+                    w.x = __float_as_uint(S[r][c * 4 + 0]);
+                    w.y = __float_as_uint(S[r][c * 4 + 1]);
+                    w.z = __float_as_uint(S[r][c * 4 + 2]);
+                    w.w = __float_as_uint(S[r][c * 4 + 3]);
+                } else {
+                    w.x = pack2<ST>(S[r][c * 8 + 0], S[r][c * 8 + 1]);
+                    w.y = pack2<ST>(S[r][c * 8 + 2], S[r][c * 8 + 3]);
+                    w.z = pack2<ST>(S[r][c * 8 + 4], S[r][c * 8 + 5]);
+                    w.w = pack2<ST>(S[r][c * 8 + 6], S[r][c * 8 + 7]);
+                }
+                *reinterpret_cast<uint4*>(
+                    wbase + (static_cast<size_t>(row) * D + c * CSTRIDE + j * EPC) * ESZ) = w;
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- gated RMSNorm over V per (token, head): y = o rsqrt(mean o^2 + eps) w silu(z)
+#pragma unroll
+    for (int i = 0; i < NTW; ++i) {
+        const int t = wave + 4 * i;
+        if (t < L) {
+            const float2 o = *reinterpret_cast<const float2*>(&sO[t][2 * lane]);
+            const float ms = sum64(o.x * o.x + o.y * o.y) * (1.0f / D);
+            const float rr = 1.0f / sqrtf(ms + p.norm_eps);
+            const float gx = zv[i].x / (1.0f + expf(-zv[i].x));
+            const float gy = zv[i].y / (1.0f + expf(-zv[i].y));
+            const float2 y = make_float2(o.x * rr * wn.x * gx, o.y * rr * wn.y * gy);
+            store_pair<OUT>(p.out, rowv[i] * p.o_st + h * p.o_sh + 2 * lane, y);
+        }
+    }
+}
+
+template <int A, int S, int O, bool SPEC>
+hipError_t launch_typed(const KParams& p, int64_t grid, hipStream_t stream)
+{
+    KParams args = p;
+    void* argv[] = {&args};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&gdn_update_kernel<A, S, O, SPEC>),
+                           dim3(static_cast<uint32_t>(grid)), dim3(NTHREADS), argv, 0, stream);
+}
+
+template <int A, int S, bool SPEC>
+hipError_t launch_out(int out, const KParams& p, int64_t grid, hipStream_t s)
+{
+    switch (out) {
+    case GDN_F32: return launch_typed<A, S, GDN_F32, SPEC>(p, grid, s);
+    case GDN_F16: return launch_typed<A, S, GDN_F16, SPEC>(p, grid, s);
+    default: return launch_typed<A, S, GDN_BF16, SPEC>(p, grid, s);
+    }
+}
+
+template <int A, bool SPEC>
+hipError_t launch_state(int st, int out, const KParams& p, int64_t grid, hipStream_t s)
+{
+    switch (st) {
+    case GDN_F32: return launch_out<A, GDN_F32, SPEC>(out, p, grid, s);
+    case GDN_F16: return launch_out<A, GDN_F16, SPEC>(out, p, grid, s);
+    default: return launch_out<A, GDN_BF16, SPEC>(out, p, grid, s);
+    }
+}
+
+template <bool SPEC>
+hipError_t launch(int act, int st, int out, const KParams& p, int64_t grid, hipStream_t s)
+{
+    switch (act) {
+    case GDN_F32: return launch_state<GDN_F32, SPEC>(st, out, p, grid, s);
+    case GDN_F16: return launch_state<GDN_F16, SPEC>(st, out, p, grid, s);
+    default: return launch_state<GDN_BF16, SPEC>(st, out, p, grid, s);
+    }
+}
+
+KParams make_params(const gdn_layer* L, const gdn_state_pool* P)
+{
+    KParams p{};
+    p.q = L->q.data; p.q_st = L->q.stride_tok; p.q_sh = L->q.stride_head;
+    p.k = L->k.data; p.k_st = L->k.stride_tok; p.k_sh = L->k.stride_head;
+    p.v = L->v.data; p.v_st = L->v.stride_tok; p.v_sh = L->v.stride_head;
+    p.z = L->z.data; p.z_st = L->z.stride_tok; p.z_sh = L->z.stride_head;
+    p.a = L->a.data; p.a_st = L->a.stride_tok;
+    p.b = L->b.data; p.b_st = L->b.stride_tok;
+    p.out = L->out.data; p.o_st = L->out.stride_tok; p.o_sh = L->out.stride_head;
+    p.A_log = L->A_log;
+    p.dt_bias = L->dt_bias;
+    p.norm_weight = L->norm_weight;
+    p.pool = P->data;
+    p.num_slots = P->num_slots;
+    p.n_tok = L->n_tok;
+    p.HV = L->num_v_heads;
+    p.group = L->num_v_heads / L->num_k_heads;
+    p.scale = L->scale;
+    p.norm_eps = L->norm_eps;
+    return p;
+}
+
+gdn_status device_status(hipError_t e)
+{
+    if (e == hipSuccess)
+        return GDN_OK;
+    return gdn::fail(GDN_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" gdn_status gdn_spec_decode_update(const gdn_layer* layer,
+                                             const gdn_state_pool* pool,
+                                             const int32_t* cu_seqlens, int32_t num_seqs,
+                                             int32_t max_q_len,
+                                             const int32_t* spec_state_indices,
+                                             int32_t spec_stride,
+                                             const int32_t* num_accepted_tokens,
+                                             const int32_t* token_indx, hipStream_t stream)
+{
+    gdn::clear_error();
+    gdn_status st;
+    if ((st = gdn::check_layer(layer)) != GDN_OK || (st = gdn::check_pool(pool)) != GDN_OK)
+        return st;
+    if (num_seqs < 0)
+        return gdn::fail(GDN_ERR_INVALID, "num_seqs is negative");
+    if (max_q_len < 1)
+        return gdn::fail(GDN_ERR_INVALID, "max_q_len must be >= 1");
+    if (max_q_len > GDN_MAX_DRAFT_TOKENS)
+        return gdn::fail(GDN_ERR_UNSUPPORTED, "max_q_len %d exceeds %d draft tokens",
+                         max_q_len, GDN_MAX_DRAFT_TOKENS);
+    if (spec_stride < 1)
+        return gdn::fail(GDN_ERR_INVALID, "spec_stride must be >= 1");
+    if (num_seqs == 0 || layer->n_tok == 0)
+        return GDN_OK;  // no sequence, or no row any sequence could use
+    if (!cu_seqlens || !spec_state_indices || !num_accepted_tokens)
+        return gdn::fail(GDN_ERR_INVALID, "spec metadata pointer is NULL");
+    const int64_t grid = static_cast<int64_t>(num_seqs) * layer->num_v_heads;
+    if (grid > 0x7fffffffLL)
+        return gdn::fail(GDN_ERR_INVALID, "num_seqs * num_v_heads exceeds the grid limit");
+    KParams p = make_params(layer, pool);
+    p.cu = cu_seqlens;
+    p.spec_idx = spec_state_indices;
+    p.num_acc = num_accepted_tokens;
+    p.tix = token_indx;
+    p.spec_stride = spec_stride;
+    return device_status(
+        launch<true>(layer->act_dtype, pool->dtype, layer->out_dtype, p, grid, stream));
+}
+
+extern "C" gdn_status gdn_decode_update(const gdn_layer* layer, const gdn_state_pool* pool,
+                                        const int32_t* state_indices, int32_t num_tokens,
+                                        const int32_t* token_indx, hipStream_t stream)
+{
+    gdn::clear_error();
+    gdn_status st;
+    if ((st = gdn::check_layer(layer)) != GDN_OK || (st = gdn::check_pool(pool)) != GDN_OK)
+        return st;
+    if (num_tokens < 0)
+        return gdn::fail(GDN_ERR_INVALID, "num_tokens is negative");
+    if (num_tokens == 0 || layer->n_tok == 0)
+        return GDN_OK;
+    if (!state_indices)
+        return gdn::fail(GDN_ERR_INVALID, "state_indices is NULL");
+    const int64_t grid = static_cast<int64_t>(num_tokens) * layer->num_v_heads;
+    if (grid > 0x7fffffffLL)
+        return gdn::fail(GDN_ERR_INVALID, "num_tokens * num_v_heads exceeds the grid limit");
+    KParams p = make_params(layer, pool);
+    p.state_idx = state_indices;
+    p.tix = token_indx;
+    p.spec_stride = 1;
+    return device_status(
+        launch<false>(layer->act_dtype, pool->dtype, layer->out_dtype, p, grid, stream));
+}

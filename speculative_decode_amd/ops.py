@@ -1,0 +1,302 @@
+"""Python binding of libgdn_spec.so: argument marshalling only.
+
+Every step of the update runs in the HIP kernels of the library; this module
+turns torch device tensors into the C structs of ``include/gdn_spec.h`` and
+enqueues on torch's current stream.  Nothing here computes, copies or casts
+tensor data, and there is no fallback: a missing library or a non-OK status
+raises.
+
+The argument list follows the fused post-conv MTP decode op of vLLM PR #51674
+(report section 关键源码片段, the ``fused_gdn_decode_post_conv_mtp`` wrapper:
+q/k/v split views, gates a/b, A_log, dt_bias, state indices, cu_seqlens,
+num_accepted_tokens, the state pool, output gate z, norm weight, out,
+scale = K**-0.5, norm_eps = 1e-5), with the speculative slot table of PR
+#46090 and the gather index of PR #51812.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn_spec.so")
+ABI_VERSION = 1
+MAX_DRAFT_TOKENS = 8
+
+GDN_F32, GDN_F16, GDN_BF16 = 0, 1, 2
+_DTYPE = {torch.float32: GDN_F32, torch.float16: GDN_F16, torch.bfloat16: GDN_BF16}
+STATUS = {0: "GDN_OK", 1: "GDN_ERR_INVALID", 2: "GDN_ERR_UNSUPPORTED", 3: "GDN_ERR_DEVICE"}
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, reason: str):
+        super().__init__(f"{STATUS.get(status, status)}: {reason}")
+        self.status = status
+        self.reason = reason
+
+
+class GdnView(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("stride_tok", ctypes.c_int64),
+                ("stride_head", ctypes.c_int64)]
+
+
+class GdnLayer(ctypes.Structure):
+    _fields_ = [("q", GdnView), ("k", GdnView), ("v", GdnView), ("z", GdnView),
+                ("a", GdnView), ("b", GdnView), ("out", GdnView),
+                ("A_log", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p),
+                ("norm_weight", ctypes.c_void_p),
+                ("act_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("num_k_heads", ctypes.c_int32), ("num_v_heads", ctypes.c_int32),
+                ("head_k_dim", ctypes.c_int32), ("head_v_dim", ctypes.c_int32),
+                ("n_tok", ctypes.c_int64), ("scale", ctypes.c_float),
+                ("norm_eps", ctypes.c_float)]
+
+
+class GdnStatePool(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("num_slots", ctypes.c_int64)]
+
+
+_lib = None
+
+# Every symbol the header declares, with its ctypes signature.
+_VP, _I32, _I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+SIGNATURES = {
+    "gdn_spec_decode_update": (ctypes.c_int, [ctypes.POINTER(GdnLayer),
+                                              ctypes.POINTER(GdnStatePool), _VP, _I32, _I32,
+                                              _VP, _I32, _VP, _VP, _VP]),
+    "gdn_decode_update": (ctypes.c_int, [ctypes.POINTER(GdnLayer),
+                                         ctypes.POINTER(GdnStatePool), _VP, _I32, _VP, _VP]),
+    "gdn_validate_indices_host": (ctypes.c_int, [_I64, _I64, _VP, _I32, _I32, _VP, _I32,
+                                                 _VP, _VP, _VP, _I32, _VP]),
+    "gdn_last_error": (ctypes.c_char_p, []),
+    "gdn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "gdn_abi_version": (ctypes.c_int32, []),
+    "gdn_abi_struct_sizes": (None, [ctypes.POINTER(ctypes.c_size_t)] * 3),
+}
+
+
+def load_library():
+    """Load libgdn_spec.so (built in-tree); raise if it is missing or its ABI
+    differs from this binding."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is not built; run `python -m speculative_decode_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if lib.gdn_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"libgdn_spec ABI {lib.gdn_abi_version()} != binding {ABI_VERSION}")
+    sizes = [ctypes.c_size_t() for _ in range(3)]
+    lib.gdn_abi_struct_sizes(*[ctypes.byref(s) for s in sizes])
+    want = [ctypes.sizeof(GdnView), ctypes.sizeof(GdnLayer), ctypes.sizeof(GdnStatePool)]
+    if [s.value for s in sizes] != want:
+        raise RuntimeError(f"struct layout mismatch: library {[s.value for s in sizes]}, "
+                           f"binding {want}")
+    _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load_library().gdn_last_error().decode()
+
+
+def _check(status: int):
+    if status != 0:
+        raise GdnError(status, last_error())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _view3(t: torch.Tensor, name: str) -> GdnView:
+    if t.dim() != 3:
+        raise ValueError(f"{name} must be [n_tok, heads, dim]")
+    if t.numel() == 0:          # no rows: strides are meaningless
+        return GdnView(None, 0, 0)
+    if t.stride(-1) != 1:
+        raise ValueError(f"{name} must have a contiguous last dim")
+    return GdnView(t.data_ptr(), t.stride(0), t.stride(1))
+
+
+def _view2(t: torch.Tensor, name: str) -> GdnView:
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be [n_tok, heads]")
+    if t.numel() == 0:
+        return GdnView(None, 0, 1)
+    if t.stride(-1) != 1:
+        raise ValueError(f"{name} must have a contiguous last dim")
+    return GdnView(t.data_ptr(), t.stride(0), 1)
+
+
+def _meta(t: Optional[torch.Tensor], name: str, device) -> Optional[torch.Tensor]:
+    if t is None:
+        return None
+    if t.dtype != torch.int32 or not t.is_contiguous() or t.device != device:
+        raise ValueError(f"{name} must be a contiguous int32 tensor on {device}")
+    return t
+
+
+def make_layer(q, k, v, z, a, b, A_log, dt_bias, norm_weight, out, *, scale=None,
+               norm_eps=1e-5) -> GdnLayer:
+    """Describe one layer's device tensors as a gdn_layer (no data is touched)."""
+    dev = q.device
+    for name, t in (("k", k), ("v", v), ("z", z), ("a", a), ("b", b), ("A_log", A_log),
+                    ("dt_bias", dt_bias), ("norm_weight", norm_weight), ("out", out)):
+        if t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, q on {dev}")
+    if not (q.dtype == k.dtype == v.dtype == z.dtype == a.dtype == b.dtype):
+        raise ValueError("q, k, v, z, a, b must share one dtype")
+    for name, t in (("A_log", A_log), ("dt_bias", dt_bias), ("norm_weight", norm_weight)):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 tensor")
+    if q.dtype not in _DTYPE or out.dtype not in _DTYPE:
+        raise ValueError("activations and out must be float32, float16 or bfloat16")
+    n_tok, HK, K = q.shape
+    HV, V = v.shape[1], v.shape[2]
+    for name, t, shp in (("k", k, (n_tok, HK, K)), ("v", v, (n_tok, HV, V)),
+                         ("z", z, (n_tok, HV, V)), ("out", out, (n_tok, HV, V)),
+                         ("a", a, (n_tok, HV)), ("b", b, (n_tok, HV))):
+        if tuple(t.shape) != shp:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shp}")
+    return GdnLayer(
+        _view3(q, "q"), _view3(k, "k"), _view3(v, "v"), _view3(z, "z"),
+        _view2(a, "a"), _view2(b, "b"), _view3(out, "out"),
+        A_log.data_ptr(), dt_bias.data_ptr(), norm_weight.data_ptr(),
+        _DTYPE[q.dtype], _DTYPE[out.dtype], HK, HV, K, V, n_tok,
+        float(K ** -0.5 if scale is None else scale), float(norm_eps))
+
+
+def make_pool(state: torch.Tensor) -> GdnStatePool:
+    if state.dtype not in _DTYPE:
+        raise ValueError("state pool must be float32, float16 or bfloat16")
+    if state.dim() != 4 or not state.is_contiguous():
+        raise ValueError("state pool must be a contiguous [num_slots, HV, V, K] tensor")
+    return GdnStatePool(state.data_ptr(), _DTYPE[state.dtype], 0, state.shape[0])
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def spec_decode_update(q, k, v, z, a, b, A_log, dt_bias, norm_weight, state,
+                       cu_seqlens, spec_state_indices, num_accepted_tokens, *,
+                       token_indx=None, out=None, scale=None, norm_eps=1e-5,
+                       max_q_len=MAX_DRAFT_TOKENS):
+    """Speculative update of ``state`` in place; returns ``out``.
+
+    ``spec_state_indices`` is ``[num_seqs, spec_stride]``.  ``out`` defaults to
+    ``torch.zeros_like(z)``: only processed rows are written.
+    """
+    lib = load_library()
+    if out is None:
+        out = torch.zeros_like(z)
+    dev = q.device
+    layer = make_layer(q, k, v, z, a, b, A_log, dt_bias, norm_weight, out,
+                       scale=scale, norm_eps=norm_eps)
+    pool = make_pool(state)
+    cu = _meta(cu_seqlens, "cu_seqlens", dev)
+    si = _meta(spec_state_indices, "spec_state_indices", dev)
+    na = _meta(num_accepted_tokens, "num_accepted_tokens", dev)
+    ti = _meta(token_indx, "token_indx", dev)
+    if si.dim() != 2:
+        raise ValueError("spec_state_indices must be [num_seqs, spec_stride]")
+    B = cu.shape[0] - 1
+    if si.shape[0] != B or na.shape[0] != B:
+        raise ValueError("cu_seqlens, spec_state_indices, num_accepted_tokens disagree on B")
+    _check(lib.gdn_spec_decode_update(ctypes.byref(layer), ctypes.byref(pool), _ptr(cu), B,
+                                      int(max_q_len), _ptr(si), si.shape[1], _ptr(na),
+                                      _ptr(ti), _stream(dev)))
+    return out
+
+
+def decode_update(q, k, v, z, a, b, A_log, dt_bias, norm_weight, state, state_indices, *,
+                  token_indx=None, out=None, scale=None, norm_eps=1e-5):
+    """Non-speculative single-token update, in place at ``state_indices[i]``
+    (negative = padding); returns ``out`` (default zeros)."""
+    lib = load_library()
+    if out is None:
+        out = torch.zeros_like(z)
+    dev = q.device
+    layer = make_layer(q, k, v, z, a, b, A_log, dt_bias, norm_weight, out,
+                       scale=scale, norm_eps=norm_eps)
+    pool = make_pool(state)
+    si = _meta(state_indices, "state_indices", dev)
+    ti = _meta(token_indx, "token_indx", dev)
+    _check(lib.gdn_decode_update(ctypes.byref(layer), ctypes.byref(pool), _ptr(si),
+                                 si.shape[0], _ptr(ti), _stream(dev)))
+    return out
+
+
+def forward_core(q, k, v, z, a, b, A_log, dt_bias, norm_weight, state, *,
+                 spec_cu_seqlens=None, spec_state_indices=None, num_accepted_tokens=None,
+                 spec_token_indx=None, non_spec_state_indices=None,
+                 non_spec_token_indx=None, out=None, scale=None, norm_eps=1e-5,
+                 max_q_len=MAX_DRAFT_TOKENS):
+    """Spec / non-spec split of one batch (vLLM PR #51812, ``_forward_core``).
+
+    A pure speculative batch passes ``spec_token_indx=None`` and runs one
+    launch with no gather.  A mixed batch gathers the spec rows (q/k/v/z *and*
+    the gates a/b, with the same index) inside the spec launch and the
+    non-spec rows inside the single-token launch; both write their own rows of
+    one ``out``.
+    """
+    if out is None:
+        out = torch.zeros_like(z)
+    if spec_cu_seqlens is not None and spec_cu_seqlens.shape[0] > 1:
+        spec_decode_update(q, k, v, z, a, b, A_log, dt_bias, norm_weight, state,
+                           spec_cu_seqlens, spec_state_indices, num_accepted_tokens,
+                           token_indx=spec_token_indx, out=out, scale=scale,
+                           norm_eps=norm_eps, max_q_len=max_q_len)
+    if non_spec_state_indices is not None and non_spec_state_indices.shape[0] > 0:
+        decode_update(q, k, v, z, a, b, A_log, dt_bias, norm_weight, state,
+                      non_spec_state_indices, token_indx=non_spec_token_indx, out=out,
+                      scale=scale, norm_eps=norm_eps)
+    return out
+
+
+def validate_indices(num_slots: int, n_tok: int, *, cu_seqlens=None, spec_state_indices=None,
+                     num_accepted_tokens=None, spec_token_indx=None, state_indices=None,
+                     non_spec_token_indx=None, max_q_len=MAX_DRAFT_TOKENS):
+    """Check the metadata contract on host copies (gdn_validate_indices_host).
+    Raises GdnError with the first violation."""
+    lib = load_library()
+
+    def host(t):
+        return None if t is None else t.detach().to("cpu", torch.int32).contiguous()
+
+    cu, si, na = host(cu_seqlens), host(spec_state_indices), host(num_accepted_tokens)
+    st, ns, nst = host(spec_token_indx), host(state_indices), host(non_spec_token_indx)
+    B = 0 if cu is None else cu.shape[0] - 1
+    stride = 1 if si is None else (si.shape[1] if si.dim() == 2 else 1)
+    _check(lib.gdn_validate_indices_host(
+        int(num_slots), int(n_tok), _ptr(cu), B, int(max_q_len), _ptr(si), stride, _ptr(na),
+        _ptr(st), _ptr(ns), 0 if ns is None else ns.shape[0], _ptr(nst)))
+
+
+def batch_args(batch, device, *, state=None, out=None):
+    """Device copies of a workloads.GDNBatch as keyword arguments of
+    forward_core (convenience for tests and the benchmark)."""
+    def d(t):
+        return None if t is None else t.to(device)
+    return dict(q=d(batch.q), k=d(batch.k), v=d(batch.v), z=d(batch.z), a=d(batch.a),
+                b=d(batch.b), A_log=d(batch.A_log), dt_bias=d(batch.dt_bias),
+                norm_weight=d(batch.norm_weight),
+                state=d(batch.pool) if state is None else state,
+                spec_cu_seqlens=d(batch.cu_seqlens),
+                spec_state_indices=d(batch.spec_state_indices),
+                num_accepted_tokens=d(batch.num_accepted_tokens),
+                spec_token_indx=d(batch.spec_token_indx),
+                non_spec_state_indices=d(batch.state_indices),
+                non_spec_token_indx=d(batch.non_spec_token_indx),
+                out=out, scale=batch.scale, norm_eps=batch.norm_eps,
+                max_q_len=max(1, batch.T))
