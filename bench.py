@@ -5,7 +5,11 @@
 One step = one launch of the whole hot path (rewind, gating, L2 norms, the
 serial recurrence over the draft tokens, every slot store, the gated-RMSNorm
 epilogue) over one batch of synthetic inputs already resident in HBM.  Steps
-run back to back on torch's current stream; the pool is updated in place.
+run back to back on torch's current stream and cycle through the state pools
+of --layers GDN layers (4 by default), as a decode step walks a model's
+layers: the pools together are several times the 256 MB Infinity Cache, so a
+step cannot find the slots it rewrites still cached from the step before.
+Every pool is updated in place.
 
 Prints one JSON line: draft tokens/s over the timed wall-clock region, the
 kernel's achieved algorithmic HBM bandwidth against the 8 TB/s peak (HIP
@@ -94,7 +98,9 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--cpu-seqs", type=int, default=32,
+    ap.add_argument("--layers", type=int, default=4,
+                    help="state pools cycled through, one per GDN layer")
+    ap.add_argument("--cpu-seqs", type=int, default=128,
                     help="sequences of the workload the CPU oracle is timed on (0: skip)")
     args = ap.parse_args()
 
@@ -115,11 +121,16 @@ def main():
           flush=True)
     kw = ops.batch_args(batch, dev)
     kw["out"] = torch.zeros((batch.n_tok, batch.HV, batch.V), dtype=batch.out_dtype, device=dev)
+    pools = [kw["state"]] + [kw["state"].clone() for _ in range(args.layers - 1)]
     tokens = batch.draft_tokens()
     alg_bytes = batch.algorithmic_bytes()
 
-    for _ in range(args.warmup):
+    def step(i):
+        kw["state"] = pools[i % len(pools)]
         ops.forward_core(**kw)
+
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
@@ -127,9 +138,9 @@ def main():
           for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for e0, e1 in ev:
+    for i, (e0, e1) in enumerate(ev):
         e0.record(stream)
-        ops.forward_core(**kw)
+        step(args.warmup + i)
         e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -162,7 +173,8 @@ def main():
                    "sequences": batch.num_seqs, "draft_tokens_per_step": tokens,
                    "HK": batch.HK, "HV": batch.HV, "K": batch.K, "V": batch.V,
                    "act_dtype": dtypes[batch.q.dtype], "state_dtype": dtypes[batch.pool.dtype],
-                   "algorithmic_bytes_per_step": alg_bytes},
+                   "algorithmic_bytes_per_step": alg_bytes, "layers_cycled": len(pools),
+                   "pool_bytes_per_layer": batch.pool.numel() * batch.pool.element_size()},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
                      "kernel_avg_us": avg_ms * 1e3, "kernel_median_us": med_ms * 1e3},

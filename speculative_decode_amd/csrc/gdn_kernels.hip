@@ -10,13 +10,15 @@
 //
 // How it is computed here (not the pages' CUDA design):
 //   * One 256-thread workgroup (4 wave64) per (sequence, value head); a 1-D
-//     grid of num_seqs*HV workgroups.
+//     grid of num_seqs*HV workgroups, mapped so each XCD works on a
+//     contiguous range of units.
 //   * The 128x128 state tile (V rows, K contiguous) lives in registers for
 //     the whole draft: each 8-lane group owns one row at a time, each lane 16
 //     of its elements, and every lane holds 4 rows (64 fp32 values).  A row
 //     chunk moves as one 16-byte access per lane, so one wave instruction
 //     covers eight full 128-byte lines.  The tile is read from HBM once and
-//     written once per draft token; nothing else touches it.
+//     written once per draft token with non-temporal stores; nothing else
+//     touches it.
 //   * Rows of S evolve independently.  Per token and row, the two dot
 //     products of the OLD row (S.k^ and S.q^) are reduced together over the
 //     8 lanes with three DPP steps; then
@@ -43,6 +45,7 @@ constexpr int NTHREADS = 256;
 constexpr int ROWS_PER_WAVE = D / (NTHREADS / 64);   // 32
 constexpr int RPT = ROWS_PER_WAVE / 8;               // rows per thread: 4
 constexpr int NE = D / 8;                            // elements per (thread, row): 16
+constexpr int NXCD = 8;                              // accelerator complex dies on MI355X
 
 struct KParams {
     const void* q;
@@ -75,6 +78,7 @@ struct KParams {
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // Raw bits of two consecutive elements: one dword for 16-bit types, two for
 // fp32.  Loads keep raw bits so that conversion waits can be deferred.
@@ -181,7 +185,7 @@ __device__ __forceinline__ float sum64(float x)
 // the speculative metadata (cu_seqlens / spec_state_indices / num_accepted)
 // or the single-token in-place form (state_indices).
 template <int ACT, int ST, int OUT, bool SPEC>
-__global__ void __launch_bounds__(NTHREADS)
+__global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(ST == GDN_F32 ? 1 : 4)))
 gdn_update_kernel(const KParams p)
 {
     constexpr int ESZ = (ST == GDN_F32) ? 4 : 2;   // state element bytes
@@ -196,7 +200,9 @@ gdn_update_kernel(const KParams p)
     __shared__ __attribute__((aligned(16))) float sQ[NT][D];
     __shared__ __attribute__((aligned(16))) float sV[NT][D];
     __shared__ __attribute__((aligned(16))) float sO[NT][D];
+    __shared__ __attribute__((aligned(16))) float sZ[NT][D];
     __shared__ float sAlpha[NT], sBeta[NT], sKQ[NT];
+    __shared__ int64_t sRow[NT];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -204,7 +210,14 @@ gdn_update_kernel(const KParams p)
     const int g = lane >> 3;   // row within the wave's 8-row band
     const int j = lane & 7;    // position within the row's 8-lane group
 
-    const int64_t unit = blockIdx.x;
+    // Workgroups are dealt to the 8 XCDs round robin (block b runs on XCD
+    // b % 8).  Give each XCD one contiguous range of units instead, so the
+    // heads of a sequence -- whose state tiles are adjacent in a slot and whose
+    // q/k rows are shared -- meet in one XCD's L2.  Bijective for any grid.
+    const int64_t nblk = gridDim.x;
+    const int64_t xcd = blockIdx.x % NXCD;
+    const int64_t per = nblk / NXCD, rem = nblk % NXCD;
+    const int64_t unit = xcd * per + (xcd < rem ? xcd : rem) + blockIdx.x / NXCD;
     const int64_t seq = unit / p.HV;
     const int h = static_cast<int>(unit - seq * p.HV);
     const int kh = h / p.group;
@@ -265,7 +278,6 @@ gdn_update_kernel(const KParams p)
     }
     const float A = -expf(p.A_log[h]);
     const float dtb = p.dt_bias[h];
-    const float2 wn = *reinterpret_cast<const float2*>(p.norm_weight + 2 * lane);
 
     // ---- the rewind tile: read once, 16 B per lane per chunk ----
     const size_t tile = static_cast<size_t>(D) * D;
@@ -281,14 +293,14 @@ gdn_update_kernel(const KParams p)
                 rbase + (static_cast<size_t>(row) * D + c * CSTRIDE + j * EPC) * ESZ);
     }
 
-    // ---- prologue compute: gates, normalised k and q, k^.q^ ----
-    float2 zv[NTW];
+    // ---- prologue compute: gates, normalised k and q, k^.q^.  Everything
+    // the epilogue needs (z, the token's row) is parked in LDS so that no
+    // register stays live across the token loop for it. ----
 #pragma unroll
     for (int i = 0; i < NTW; ++i) {
         const int t = wave + 4 * i;
         const float2 qv = unpack_pair<ACT>(qr[i]);
         const float2 kv = unpack_pair<ACT>(kr[i]);
-        zv[i] = unpack_pair<ACT>(zr[i]);
         const float nq = sum64(qv.x * qv.x + qv.y * qv.y);
         const float nk = sum64(kv.x * kv.x + kv.y * kv.y);
         const float rk = 1.0f / sqrtf(nk + 1e-6f);
@@ -300,7 +312,9 @@ gdn_update_kernel(const KParams p)
             *reinterpret_cast<float2*>(&sK[t][2 * lane]) = kn;
             *reinterpret_cast<float2*>(&sQ[t][2 * lane]) = qn;
             *reinterpret_cast<float2*>(&sV[t][2 * lane]) = unpack_pair<ACT>(vr[i]);
+            *reinterpret_cast<float2*>(&sZ[t][2 * lane]) = unpack_pair<ACT>(zr[i]);
             if (lane == 0) {
+                sRow[t] = rowv[i];
                 const float x = unpack_one<ACT>(ar[i]) + dtb;
                 const float sp = x > 20.0f ? x : log1pf(expf(x));
                 sAlpha[t] = expf(A * sp);
@@ -390,25 +404,34 @@ gdn_update_kernel(const KParams p)
                     w.z = pack2<ST>(S[r][c * 8 + 4], S[r][c * 8 + 5]);
                     w.w = pack2<ST>(S[r][c * 8 + 6], S[r][c * 8 + 7]);
                 }
-                *reinterpret_cast<uint4*>(
-                    wbase + (static_cast<size_t>(row) * D + c * CSTRIDE + j * EPC) * ESZ) = w;
+                // Streaming store: the tile is not read again in this launch,
+                // so it should not displace anything in L2 / MALL.
+                const u32x4 wv = {w.x, w.y, w.z, w.w};
+                __builtin_nontemporal_store(wv, reinterpret_cast<u32x4*>(
+                    wbase + (static_cast<size_t>(row) * D + c * CSTRIDE + j * EPC) * ESZ));
             }
         }
     }
     __syncthreads();
 
     // ---- gated RMSNorm over V per (token, head): y = o rsqrt(mean o^2 + eps) w silu(z)
+    // The lane id is taken afresh (mbcnt) so that no prologue address is kept
+    // alive across the token loop for the epilogue's benefit.
+    const int el = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const float2 wn = *reinterpret_cast<const float2*>(p.norm_weight + 2 * el);
 #pragma unroll
     for (int i = 0; i < NTW; ++i) {
         const int t = wave + 4 * i;
         if (t < L) {
-            const float2 o = *reinterpret_cast<const float2*>(&sO[t][2 * lane]);
+            const float2 o = *reinterpret_cast<const float2*>(&sO[t][2 * el]);
+            const float2 zv = *reinterpret_cast<const float2*>(&sZ[t][2 * el]);
+            const int64_t row = sRow[t];
             const float ms = sum64(o.x * o.x + o.y * o.y) * (1.0f / D);
             const float rr = 1.0f / sqrtf(ms + p.norm_eps);
-            const float gx = zv[i].x / (1.0f + expf(-zv[i].x));
-            const float gy = zv[i].y / (1.0f + expf(-zv[i].y));
+            const float gx = zv.x / (1.0f + expf(-zv.x));
+            const float gy = zv.y / (1.0f + expf(-zv.y));
             const float2 y = make_float2(o.x * rr * wn.x * gx, o.y * rr * wn.y * gy);
-            store_pair<OUT>(p.out, rowv[i] * p.o_st + h * p.o_sh + 2 * lane, y);
+            store_pair<OUT>(p.out, row * p.o_st + h * p.o_sh + 2 * el, y);
         }
     }
 }
