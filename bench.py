@@ -1,6 +1,6 @@
 """Benchmark of the fused GDN speculative-decode update on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C3b]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mtp_b128_bf16]
 
 One step = one launch of the whole hot path (rewind, gating, L2 norms, the
 serial recurrence over the draft tokens, every slot store, the gated-RMSNorm
@@ -31,7 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, AMD's published figure
-DEFAULT_WORKLOAD = "C3b"
+DEFAULT_WORKLOAD = "mtp_b128_bf16"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "speculative_decode_amd", "csrc", f)
                   for f in ("gdn_kernels.hip", "gdn_host.cpp", "gdn_internal.h")]
@@ -100,12 +100,15 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--layers", type=int, default=4,
                     help="state pools cycled through, one per GDN layer")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="instead of the benchmark, run --steps plain device copies of MIB "
+                         "MiB each (reference kernel for scaling HBM byte counters)")
     ap.add_argument("--cpu-seqs", type=int, default=128,
                     help="sequences of the workload the CPU oracle is timed on (0: skip)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build measures one GPU only; the update shards by "
+        print("bench.py measures one GPU only; the update shards by "
               "(sequence, value head) with no exchange, so there is no multi-GPU "
               "step to time.  Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
@@ -115,6 +118,15 @@ def main():
     from speculative_decode_amd import ops, workloads
 
     dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "copies": args.steps}), flush=True)
+        return
     ops.load_library()
     batch = workloads.make(args.workload)
     print(f"bench: {args.workload}: {workloads.DESCRIPTIONS[args.workload]}", file=sys.stderr,

@@ -187,8 +187,9 @@ typedef struct {
  * One draft token of the recurrence for the unit (head h) whose carry is
  * w->S, followed by the slot store and the gated-RMSNorm epilogue.
  *
- * Order ([51674] 实现拆解 1; [46090] spec kernel comments "update the state
- * and write output", "store the updated state to this token's slot"):
+ * Order ([51674] 实现拆解 1; [46090] spec kernel excerpt, whose per-token
+ * steps update the state, produce the output, then store the state in the
+ * token's own slot):
  *   S <- alpha * S                      decay first (reading: only this order
  *                                       makes beta=1 retrieve v exactly)
  *   d <- beta * (v - S k^)              delta toward v along k^

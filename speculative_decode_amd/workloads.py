@@ -207,30 +207,34 @@ def mixed_batch(*, n_non_spec, n_spec, T, HK, HV, K=128, V=128, act="bf16",
         T=T, scale=K ** -0.5)
 
 
-# The decode workloads.  C1 is the small case the oracle finishes at once;
-# C3b (B=128, T=8, BF16 state) is the headline measurement.
+# The decode workloads, named by shape.  "tiny" is small enough for the
+# oracle to check whole in well under a second; "mtp_b128_bf16" (B=128, T=8,
+# BF16 state) is the headline measurement.
 CONFIGS = {
-    "C1": dict(kind="spec", B=2, T=3, HK=1, HV=8, act="f32", state="f32",
-               num_slots=8, pool_std=0.1, acc_lo=0, acc_hi=3, seed=0),
-    "C2": dict(kind="spec", B=32, T=4, HK=4, HV=32, act="bf16", state="bf16",
-               acc_lo=1, acc_hi=4, seed=2),
-    "C3": dict(kind="spec", B=128, T=8, HK=4, HV=32, act="bf16", state="f32",
-               acc_lo=0, acc_hi=8, seed=3),
-    "C3b": dict(kind="spec", B=128, T=8, HK=4, HV=32, act="bf16", state="bf16",
-                acc_lo=0, acc_hi=8, seed=3),
-    "C4": dict(kind="mixed", n_non_spec=64, n_spec=64, T=4, HK=4, HV=32,
-               act="bf16", state="bf16", acc_lo=0, acc_hi=4, seed=4),
-    "C5": dict(kind="spec", B=512, T=8, HK=16, HV=32, act="bf16", state="f16",
-               acc_lo=1, acc_hi=8, seed=5),
+    "tiny": dict(kind="spec", B=2, T=3, HK=1, HV=8, act="f32", state="f32",
+                 num_slots=8, pool_std=0.1, acc_lo=0, acc_hi=3, seed=0),
+    "mtp_b32": dict(kind="spec", B=32, T=4, HK=4, HV=32, act="bf16", state="bf16",
+                    acc_lo=1, acc_hi=4, seed=2),
+    "mtp_b128_f32": dict(kind="spec", B=128, T=8, HK=4, HV=32, act="bf16", state="f32",
+                         acc_lo=0, acc_hi=8, seed=3),
+    "mtp_b128_bf16": dict(kind="spec", B=128, T=8, HK=4, HV=32, act="bf16", state="bf16",
+                          acc_lo=0, acc_hi=8, seed=3),
+    "mixed_b128": dict(kind="mixed", n_non_spec=64, n_spec=64, T=4, HK=4, HV=32,
+                       act="bf16", state="bf16", acc_lo=0, acc_hi=4, seed=4),
+    "large_b512_f16": dict(kind="spec", B=512, T=8, HK=16, HV=32, act="bf16", state="f16",
+                           acc_lo=1, acc_hi=8, seed=5),
 }
 
 DESCRIPTIONS = {
-    "C1": "tiny spec step: B=2 T=3 HK=1 HV=8 K=V=128, fp32, 8-slot FP32 pool",
-    "C2": "MTP small batch: B=32 T=4 HK=4 HV=32 K=V=128, bf16, BF16 pool",
-    "C3": "MTP headline: B=128 T=8 HK=4 HV=32 K=V=128, bf16, FP32 pool, acc 0..8",
-    "C3b": "MTP headline: B=128 T=8 HK=4 HV=32 K=V=128, bf16, BF16 pool, acc 0..8",
-    "C4": "mixed: 64 non-spec T=1 + 64 spec T=4, HK=4 HV=32, bf16, BF16 pool",
-    "C5": "large batch: B=512 T=8 HK=16 HV=32 K=V=128, bf16, FP16 pool",
+    "tiny": "spec step B=2 T=3 HK=1 HV=8 K=V=128, fp32 activations, FP32 pool of 8 slots",
+    "mtp_b32": "MTP decode B=32 T=4 HK=4 HV=32 K=V=128, bf16 activations, BF16 pool",
+    "mtp_b128_f32": "MTP decode B=128 T=8 HK=4 HV=32 K=V=128, bf16 activations, FP32 pool, "
+                    "acc 0..8",
+    "mtp_b128_bf16": "MTP decode B=128 T=8 HK=4 HV=32 K=V=128, bf16 activations, BF16 pool, "
+                     "acc 0..8",
+    "mixed_b128": "mixed batch: 64 non-spec T=1 + 64 spec T=4, HK=4 HV=32 K=V=128, bf16, "
+                  "BF16 pool",
+    "large_b512_f16": "decode B=512 T=8 HK=16 HV=32 K=V=128, bf16 activations, FP16 pool",
 }
 
 

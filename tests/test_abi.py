@@ -158,7 +158,7 @@ def _validate(batch, num_slots=None, **over):
 
 
 def test_validator_accepts_generated_workloads(lib):
-    for name in ("C1", "C2"):
+    for name in ("tiny", "mtp_b32"):
         _validate(workloads.make(name))
     _validate(workloads.mixed_batch(n_non_spec=5, n_spec=4, T=3, HK=1, HV=2, K=8, V=8,
                                     act="f32", state="f32", seed=1))

@@ -129,16 +129,16 @@ def check_full(batch, dev, *, pool=None):
 # small workloads, compared whole
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("seed", [0, 1, 2, 3])
-def test_c1_tiny(dev, seed):
-    check_full(workloads.make("C1", seed=seed), dev)
+def test_tiny(dev, seed):
+    check_full(workloads.make("tiny", seed=seed), dev)
 
 
-def test_c2_small_batch(dev):
-    check_full(workloads.make("C2"), dev)
+def test_mtp_b32(dev):
+    check_full(workloads.make("mtp_b32"), dev)
 
 
-def test_c4_mixed_batch(dev):
-    b = workloads.make("C4")
+def test_mixed_b128(dev):
+    b = workloads.make("mixed_b128")
     assert not torch.equal(b.spec_token_indx, torch.arange(b.spec_token_indx.numel(),
                                                            dtype=torch.int32))
     check_full(b, dev)
@@ -191,7 +191,7 @@ def test_empty_batch_is_a_no_op(dev):
 # exact invariants on the GPU path itself
 # --------------------------------------------------------------------------
 def test_deterministic_and_batch_independent(dev):
-    b = workloads.make("C2")
+    b = workloads.make("mtp_b32")
     p1, o1 = run_gpu(b, dev)
     p2, o2 = run_gpu(b, dev)
     assert torch.equal(p1, p2) and torch.equal(o1, o2)
@@ -210,7 +210,7 @@ def test_deterministic_and_batch_independent(dev):
 
 
 def test_gather_equals_pregathered(dev):
-    b = workloads.make("C4")
+    b = workloads.make("mixed_b128")
     p1, o1 = run_gpu(b, dev)
     g = b.spec_token_indx.long()
     pre = copy.copy(b)
@@ -389,6 +389,6 @@ def check_sampled(name, dev):
     print(f"[{name}] sampled {len(seqs)} sequences: out rel L2 {err:.2e}", flush=True)
 
 
-@pytest.mark.parametrize("name", ["C3", "C3b", "C5"])
+@pytest.mark.parametrize("name", ["mtp_b128_f32", "mtp_b128_bf16", "large_b512_f16"])
 def test_full_size_sampled(dev, name):
     check_sampled(name, dev)

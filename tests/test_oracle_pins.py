@@ -135,10 +135,10 @@ def test_p13_dense_form(K, V, HK, HV, B, T, seed):
 # #51674 item 1: rewind to the last accepted slot, store every token).
 # --------------------------------------------------------------------------
 def test_p1_touched_set_bruteforce():
-    base = workloads.make("C1")
+    base = workloads.make("tiny")
     T = base.T
     for L, acc in itertools.product(range(T + 1), range(T + 1)):
-        bt = workloads.make("C1")
+        bt = workloads.make("tiny")
         cu = [0, L, L + T]
         bt.q, bt.k, bt.v, bt.z, bt.a, bt.b = (x[: L + T] for x in
                                               (base.q, base.k, base.v, base.z, base.a, base.b))
@@ -156,15 +156,15 @@ def test_p1_touched_set_bruteforce():
 
 
 def test_p2_clamp_acc0_equals_acc1():
-    bt0 = workloads.make("C1")
+    bt0 = workloads.make("tiny")
     bt0.num_accepted_tokens = torch.tensor([0, 0], dtype=torch.int32)
-    bt1 = workloads.make("C1")
+    bt1 = workloads.make("tiny")
     bt1.num_accepted_tokens = torch.tensor([1, 1], dtype=torch.int32)
     p0, o0 = orc_spec(bt0)
     p1, o1 = orc_spec(bt1)
     assert bitwise_equal(p0, p1) and bitwise_equal(o0, o1)
     # and acc=2 reads a different slot, so the clamp is what makes them equal
-    bt2 = workloads.make("C1")
+    bt2 = workloads.make("tiny")
     bt2.num_accepted_tokens = torch.tensor([2, 2], dtype=torch.int32)
     p2, _ = orc_spec(bt2)
     assert not bitwise_equal(p0, p2)
