@@ -58,6 +58,9 @@
  *     Distinct write slots, and no read slot of one sequence equal to a write
  *     slot of another, are the caller's contract (data races otherwise);
  *     gdn_validate_indices_host() checks all of it on host copies.
+ *   - The pool and `out` must not overlap each other or any input: the
+ *     metadata, q/k/v/z/a/b and the parameters are read-only for the whole
+ *     launch.
  */
 #ifndef GDN_SPEC_H
 #define GDN_SPEC_H

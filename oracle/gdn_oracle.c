@@ -60,7 +60,8 @@ enum { ORC_OK = 0, ORC_BAD_ARG = 1, ORC_BAD_INDEX = 2, ORC_NO_MEMORY = 3 };
 /*
  * Nearest value to x that the binary format `fmt` can hold, ties to even
  * (IEEE 754 roundTiesToEven), with gradual underflow and overflow to +-inf.
- * The reports fix only "compute in FP32, store narrow" ([52191] 实现拆解 4);
+ * The reports fix only that arithmetic is wide and storage narrow ([52191]
+ * 实现拆解 4);
  * round-to-nearest-even is the IEEE default and the plainest reading.
  *
  *   format  significant bits  smallest normal  subnormal spacing  largest finite
@@ -119,7 +120,7 @@ static double silu(double x)
 /*
  * Gate scalars for one (token row, v-head).
  * [46090] passes A_log, a, dt_bias, b and a softplus threshold to the fused
- * "sigmoid gating" update; [52191] 实现拆解 4 scales the state by exp(g).
+ * sigmoid-gating update; [52191] 实现拆解 4 scales the state by exp(g).
  * Reading: g = -exp(A_log) * softplus(a + dt_bias) so alpha = exp(g) is a
  * decay in (0, 1]; beta = sigmoid(b) is the write strength in (0, 1).
  */

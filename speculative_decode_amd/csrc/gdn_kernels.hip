@@ -11,7 +11,8 @@
 // How it is computed here (not the pages' CUDA design):
 //   * One 256-thread workgroup (4 wave64) per (sequence, value head); a 1-D
 //     grid of num_seqs*HV workgroups, mapped so each XCD works on a
-//     contiguous range of units.
+//     contiguous range of units.  Batches above one round of resident
+//     blocks run one block per CU (an LDS reservation caps occupancy).
 //   * The 128x128 state tile (V rows, K contiguous) lives in registers for
 //     the whole draft: each 8-lane group owns one row at a time, each lane 16
 //     of its elements, and every lane holds 4 rows (64 fp32 values).  A row
@@ -33,6 +34,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 #include <type_traits>
 
 #include "gdn_internal.h"
@@ -436,13 +438,87 @@ gdn_update_kernel(const KParams p)
     }
 }
 
+// ---- launch planning ---------------------------------------------------------
+// Per-device figures the plan needs, queried once per device.
+struct DeviceInfo {
+    int cus = 0;
+    int lds_per_cu = 0;
+    int lds_per_block = 0;
+};
+
+hipError_t device_info(DeviceInfo* out)
+{
+    constexpr int MAX_DEVICES = 64;
+    static std::mutex mu;
+    static DeviceInfo cache[MAX_DEVICES];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    const bool cacheable = dev >= 0 && dev < MAX_DEVICES;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cacheable && cache[dev].cus > 0) {
+        *out = cache[dev];
+        return hipSuccess;
+    }
+    DeviceInfo d;
+    if ((e = hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev)) ||
+        (e = hipDeviceGetAttribute(&d.lds_per_cu,
+                                   hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev)) ||
+        (e = hipDeviceGetAttribute(&d.lds_per_block, hipDeviceAttributeMaxSharedMemoryPerBlock,
+                                   dev)))
+        return e;
+    if (cacheable)
+        cache[dev] = d;
+    *out = d;
+    return hipSuccess;
+}
+
+// Static LDS of one block: k^, q^, v, o, z rows plus the per-token scalars.
+constexpr size_t static_lds_bytes(int nt)
+{
+    return size_t(5) * nt * D * sizeof(float) + size_t(3) * nt * sizeof(float) +
+           size_t(nt) * sizeof(int64_t);
+}
+
+// Blocks resident per CU before a batch counts as large.
+constexpr int ROUND_BLOCKS_PER_CU = 4;
+
+// Dynamic LDS to reserve for a launch of nunits blocks.  Each block writes up
+// to eight scattered state tiles for the one it reads.  With several such
+// blocks per CU, the write streams of the whole chip land on more DRAM rows
+// at once than the memory keeps open, and the sustained rate drops.  So once
+// a batch is larger than one round of resident blocks, the launch reserves
+// LDS that the kernel never touches -- just over half a CU's -- so that one
+// block runs per CU.  The stores of a finishing block still drain while the
+// CU's next block loads.  A smaller batch keeps every unit resident at once.
+template <int NT>
+hipError_t plan_lds(int64_t nunits, size_t* lds)
+{
+    *lds = 0;
+    DeviceInfo d;
+    hipError_t e = device_info(&d);
+    if (e != hipSuccess)
+        return e;
+    if (nunits <= static_cast<int64_t>(d.cus) * ROUND_BLOCKS_PER_CU)
+        return hipSuccess;
+    const size_t half = static_cast<size_t>(d.lds_per_cu) / 2 + 1;
+    if (half + static_lds_bytes(NT) <= static_cast<size_t>(d.lds_per_block))
+        *lds = half;
+    return hipSuccess;
+}
+
 template <int A, int S, int O, bool SPEC>
 hipError_t launch_typed(const KParams& p, int64_t grid, hipStream_t stream)
 {
+    size_t lds = 0;
+    hipError_t e = plan_lds<SPEC ? MAXT : 1>(grid, &lds);
+    if (e != hipSuccess)
+        return e;
     KParams args = p;
     void* argv[] = {&args};
     return hipLaunchKernel(reinterpret_cast<const void*>(&gdn_update_kernel<A, S, O, SPEC>),
-                           dim3(static_cast<uint32_t>(grid)), dim3(NTHREADS), argv, 0, stream);
+                           dim3(static_cast<uint32_t>(grid)), dim3(NTHREADS), argv, lds, stream);
 }
 
 template <int A, int S, bool SPEC>

@@ -392,3 +392,26 @@ def check_sampled(name, dev):
 @pytest.mark.parametrize("name", ["mtp_b128_f32", "mtp_b128_bf16", "large_b512_f16"])
 def test_full_size_sampled(dev, name):
     check_sampled(name, dev)
+
+
+# --------------------------------------------------------------------------
+# batches above one round of resident blocks launch with an LDS reservation
+# that holds one block per CU; ragged and skipped units must be unaffected
+# --------------------------------------------------------------------------
+def test_capped_launch_ragged_spec(dev):
+    """1,152 units (> 4 per CU on 256 CUs): ragged lengths 0..8 and every
+    acceptance count, in the capped launch."""
+    B = 36
+    lens = [(3 * i) % 9 for i in range(B)]
+    b = workloads.spec_batch(B=B, T=8, HK=4, HV=32, act="bf16", state="bf16", q_lens=lens,
+                             acc_lo=0, acc_hi=8, seed=21)
+    check_full(b, dev)
+
+
+def test_capped_launch_nonspec(dev):
+    """A single-token batch of 40 entries x 32 heads (1,280 units) with padding."""
+    b = workloads.mixed_batch(n_non_spec=40, n_spec=0, T=1, HK=4, HV=32, act="bf16",
+                              state="f32", seed=22)
+    b.state_indices[7] = -1
+    b.state_indices[31] = -1
+    check_full(b, dev)
