@@ -1,12 +1,14 @@
-"""CPU oracle of the GDN speculative-decode state update -- TEST INFRASTRUCTURE.
+"""CPU oracle of the GDN speculative-decode state update and of the conv
+update that precedes it -- TEST INFRASTRUCTURE.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package.  The product path (the HIP library and
 its Python binding) never imports, links or calls anything here, and nothing
 here imports the product package.
 
-The arithmetic lives in ``gdn_oracle.c`` (plain serial C, every operation in
-double); this module only marshals torch/numpy arrays into it:
+The arithmetic lives in ``gdn_oracle.c`` and ``conv_oracle.c`` (plain serial
+C, every operation in double); this module only marshals torch/numpy arrays
+into them:
 inputs of any float dtype are upcast exactly to float64, the C code rounds to
 the storage format at each slot/output write, and the results are cast back
 to the caller's dtypes (exact, because the values are already representable).
@@ -21,7 +23,7 @@ import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "gdn_oracle.c")
+_SRCS = [os.path.join(_HERE, "gdn_oracle.c"), os.path.join(_HERE, "conv_oracle.c")]
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 FMT_F32, FMT_F16, FMT_BF16, FMT_F64 = 0, 1, 2, 3
@@ -36,7 +38,7 @@ def build() -> str:
     """Compile liboracle.so with gcc (no FMA contraction, no fast-math)."""
     tmp = _LIB_PATH + ".tmp"
     cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-ffp-contract=off",
-           "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+           "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp] + _SRCS + ["-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
@@ -59,6 +61,9 @@ def _load():
     lib.orc_decode_update.restype = ctypes.c_int
     lib.orc_decode_update.argtypes = common_head + [vp, i32, vp,
                                                     i32, i32, i32, i32, d, d]
+    lib.orc_conv_update.restype = ctypes.c_int
+    lib.orc_conv_update.argtypes = [vp, vp, ctypes.c_int, vp, ctypes.c_int, i64, i32, i64,
+                                    i32, i32, vp, vp, i32, vp, i32, vp, vp, vp]
     _lib = lib
     return lib
 
@@ -149,3 +154,50 @@ def decode_update(q, k, v, z, a, b, A_log, dt_bias, norm_weight, pool,
         raise ValueError(f"oracle decode_update: {_ERR.get(rc, rc)}")
     return (torch.from_numpy(pool64).to(pool.dtype),
             torch.from_numpy(out64).to(odt))
+
+
+CONV_ACT = {None: 0, "none": 0, "silu": 1}
+
+
+def _conv_call(x, weight, bias, cache, cu, lines, num_acc, token_indx, out, out_dtype,
+               activation, B):
+    n_tok, C = x.shape
+    num_lines, state_len, C2 = cache.shape
+    Cw, width = weight.shape
+    assert C2 == C and Cw == C
+    if out is None:
+        out = torch.zeros((n_tok, C), dtype=out_dtype or x.dtype)
+    odt = out.dtype
+    x64, w64 = _f64(x), _f64(weight)
+    b64 = None if bias is None else _f64(bias)
+    out64, cache64 = _f64(out).copy(), _f64(cache).copy()
+    rc = _load().orc_conv_update(
+        _p(x64), _p(out64), _FMT[odt], _p(cache64), _FMT[cache.dtype], num_lines, state_len,
+        n_tok, C, width, _p(w64), _p(b64), CONV_ACT[activation], _p(cu), B, _p(lines),
+        _p(num_acc), _p(token_indx))
+    if rc:
+        raise ValueError(f"oracle conv update: {_ERR.get(rc, rc)}")
+    return torch.from_numpy(cache64).to(cache.dtype), torch.from_numpy(out64).to(odt)
+
+
+def conv_spec_update(x, weight, bias, cache, cu_seqlens, conv_indices, num_accepted_tokens,
+                     *, token_indx=None, out=None, out_dtype=None, activation="silu"):
+    """Speculative conv update with rewind; returns ``(cache_after, out_after)``.
+
+    ``x`` is ``[n_tok, C]``, ``weight`` ``[C, width]``, ``cache``
+    ``[num_lines, state_len, C]`` (any strides; the result is contiguous).
+    ``conv_indices[b]`` is the buffer line of sequence b.  Inputs are not
+    modified.
+    """
+    cu = _i32(cu_seqlens)
+    return _conv_call(x, weight, bias, cache, cu, _i32(conv_indices),
+                      _i32(num_accepted_tokens), _i32(token_indx), out, out_dtype, activation,
+                      cu.shape[0] - 1)
+
+
+def conv_decode_update(x, weight, bias, cache, conv_indices, *, token_indx=None, out=None,
+                       out_dtype=None, activation="silu"):
+    """Non-speculative single-token conv update (a negative line is padding)."""
+    lines = _i32(conv_indices)
+    return _conv_call(x, weight, bias, cache, None, lines, None, _i32(token_indx), out,
+                      out_dtype, activation, lines.shape[0])

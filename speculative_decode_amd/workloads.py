@@ -238,6 +238,129 @@ DESCRIPTIONS = {
 }
 
 
+@dataclass
+class ConvBatch:
+    """Inputs of the conv update that precedes the recurrent update (CPU
+    tensors).  ``x`` holds the conv inputs (the packed q/k/v projection before
+    the conv) of every row; ``cache`` is the wide rolling conv buffer,
+    ``[num_lines, state_len, C]``; sequence b owns line ``conv_indices[b]``."""
+    name: str
+    x: torch.Tensor                     # [n_tok, C]
+    weight: torch.Tensor                # [C, width] fp32
+    bias: Optional[torch.Tensor]        # [C] fp32 or None
+    cache: torch.Tensor                 # [num_lines, state_len, C]
+    out_dtype: torch.dtype
+    cu_seqlens: torch.Tensor            # int32 [B+1]
+    conv_indices: torch.Tensor          # int32 [B]
+    num_accepted_tokens: torch.Tensor   # int32 [B]
+    token_indx: Optional[torch.Tensor] = None
+    activation: str = "silu"
+    T: int = 0
+
+    @property
+    def n_tok(self) -> int:
+        return self.x.shape[0]
+
+    @property
+    def channels(self) -> int:
+        return self.x.shape[1]
+
+    @property
+    def width(self) -> int:
+        return self.weight.shape[1]
+
+    @property
+    def state_len(self) -> int:
+        return self.cache.shape[1]
+
+    @property
+    def num_seqs(self) -> int:
+        return self.cu_seqlens.shape[0] - 1
+
+    def draft_tokens(self) -> int:
+        return int(self.cu_seqlens[-1])
+
+    def algorithmic_bytes(self) -> int:
+        """Per active sequence: read width-1 history positions and L inputs,
+        write L outputs and width-2+L buffer positions; plus the weight and
+        bias once and the metadata."""
+        C, W = self.channels, self.width
+        s_c, s_x = self.cache.element_size(), self.x.element_size()
+        s_o = torch.empty((), dtype=self.out_dtype).element_size()
+        lens = (self.cu_seqlens[1:] - self.cu_seqlens[:-1]).clamp(min=0)
+        active = lens > 0
+        n_act, rows = int(active.sum()), int(lens.sum())
+        data = (n_act * (W - 1) * C * s_c + rows * C * s_x + rows * C * s_o
+                + int(((W - 2 + lens) * active).sum()) * C * s_c)
+        params = C * W * 4 + (0 if self.bias is None else C * 4)
+        meta = 4 * (self.cu_seqlens.numel() + 2 * self.num_seqs)
+        if self.token_indx is not None:
+            meta += 4 * self.token_indx.numel()
+        return data + params + meta
+
+
+def conv_batch(*, B, T, C, width=4, state_len=None, dtype="bf16", out=None, num_lines=None,
+               acc_lo=0, acc_hi=None, q_lens=None, bias=True, activation="silu", gather=False,
+               seed=0, name="conv") -> ConvBatch:
+    """B sequences of up to T draft rows over C channels.
+
+    Draw order: x ~ N(0, 1), weight ~ U(-0.5, 0.5) ([C, width]), bias ~
+    U(-0.5, 0.5), the buffer ~ N(0, 1) line by line, the line permutation,
+    num_accepted ~ U{acc_lo..acc_hi}, and (gather=True) a row permutation used
+    as token_indx.  state_len defaults to width - 2 + T, the least that holds
+    a rewound history plus T new inputs.
+    """
+    acc_hi = T if acc_hi is None else acc_hi
+    state_len = width - 2 + T if state_len is None else state_len
+    num_lines = B if num_lines is None else num_lines
+    assert num_lines >= B
+    lens = np.full(B, T, dtype=np.int64) if q_lens is None else np.asarray(q_lens, np.int64)
+    assert lens.shape == (B,) and (lens <= T).all()
+    cu = np.zeros(B + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(np.maximum(lens, 0))
+    n_tok = int(cu[-1])
+    rng = np.random.Generator(np.random.PCG64(seed))
+    dt = _DT[dtype]
+    x = _draw_act(rng, (n_tok, C), dt)
+    weight = torch.from_numpy(rng.uniform(-0.5, 0.5, (C, width)).astype(np.float32))
+    b = torch.from_numpy(rng.uniform(-0.5, 0.5, C).astype(np.float32)) if bias else None
+    cache = torch.empty((num_lines, state_len, C), dtype=dt)
+    for ln in range(num_lines):
+        cache[ln] = _draw_act(rng, (state_len, C), dt)
+    perm = rng.permutation(num_lines).astype(np.int32)
+    acc = rng.integers(acc_lo, acc_hi + 1, size=B).astype(np.int32)
+    tix = None
+    if gather:
+        tix = torch.from_numpy(rng.permutation(n_tok).astype(np.int32))
+    return ConvBatch(name=name, x=x, weight=weight, bias=b, cache=cache,
+                     out_dtype=_DT[out or dtype], cu_seqlens=torch.from_numpy(cu),
+                     conv_indices=torch.from_numpy(perm[:B].copy()),
+                     num_accepted_tokens=torch.from_numpy(acc), token_indx=tix,
+                     activation=activation, T=T)
+
+
+# Conv workloads.  C = 2*HK*K + HV*V channels (q, k and v of the GDN layer
+# whose update follows), width 4, a buffer of width - 2 + T positions.
+CONV_CONFIGS = {
+    "conv_tiny": dict(B=3, T=3, C=40, width=4, dtype="f32", num_lines=6, acc_lo=0, acc_hi=3,
+                      seed=10),
+    "conv_mtp_b128": dict(B=128, T=8, C=2 * 4 * 128 + 32 * 128, width=4, dtype="bf16",
+                          num_lines=256, acc_lo=0, acc_hi=8, seed=11),
+}
+
+CONV_DESCRIPTIONS = {
+    "conv_tiny": "conv update B=3 T=3 C=40 width 4, fp32, 6 buffer lines",
+    "conv_mtp_b128": "conv update B=128 T=8 C=5120 (HK=4 HV=32 K=V=128) width 4, bf16 "
+                     "inputs/buffer/outputs, SiLU, acc 0..8",
+}
+
+
+def make_conv(name: str, **overrides) -> ConvBatch:
+    cfg = dict(CONV_CONFIGS[name])
+    cfg.update(overrides)
+    return conv_batch(name=name, **cfg)
+
+
 def make(name: str, **overrides) -> GDNBatch:
     cfg = dict(CONFIGS[name])
     cfg.update(overrides)
