@@ -1,6 +1,7 @@
 """Benchmark of the fused GDN speculative-decode update on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mtp_b128_bf16]
+    python bench.py --path conv [--workload conv_mtp_b128]
 
 One step = one launch of the whole hot path (rewind, gating, L2 norms, the
 serial recurrence over the draft tokens, every slot store, the gated-RMSNorm
@@ -11,12 +12,20 @@ layers: the pools together are several times the 256 MB Infinity Cache, so a
 step cannot find the slots it rewrites still cached from the step before.
 Every pool is updated in place.
 
-Prints one JSON line: draft tokens/s over the timed wall-clock region, the
-kernel's achieved algorithmic HBM bandwidth against the 8 TB/s peak (HIP
-events around every timed launch, on the launch stream), the HBM traffic that
+Prints one JSON line: draft tokens/s over the timed region (HIP events around
+all timed steps, which the host has enqueued ahead of the GPU), the
+kernel's achieved algorithmic HBM bandwidth against the 8 TB/s peak (the
+average launch duration from those events, on the launch stream; a second
+pass with an event pair around every launch gives the percentiles), the HBM
+traffic that
 rocprofv3 counters recorded for the same kernel build (if the recording
 matches the current kernel source), and the CPU oracle timed on a bounded
 sample of the same workload.
+
+--path conv times the conv update with rewind that precedes the recurrent
+update instead (the same JSON fields), cycling each layer's own buffer,
+inputs and outputs over 32 layers by default so that nothing it reads is
+still cached from the previous use of that layer.
 """
 from __future__ import annotations
 
@@ -31,21 +40,27 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, AMD's published figure
-DEFAULT_WORKLOAD = "mtp_b128_bf16"
+DEFAULT_WORKLOAD = {"gdn": "mtp_b128_bf16", "conv": "conv_mtp_b128"}
+DEFAULT_LAYERS = {"gdn": 4, "conv": 32}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "speculative_decode_amd", "csrc", f)
-                  for f in ("gdn_kernels.hip", "gdn_host.cpp", "gdn_internal.h")]
+_CSRC = os.path.join(ROOT, "speculative_decode_amd", "csrc")
+KERNEL_SOURCES = {
+    "gdn": ["gdn_kernels.hip", "gdn_host.cpp"],
+    "conv": ["conv_kernels.hip", "conv_host.cpp"],
+}
+SHARED_SOURCES = ["gdn_internal.h", "dtype_cvt.h"]
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(path: str = "gdn") -> str:
+    """Hash of the sources that build the kernel of ``path``."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
+    for name in KERNEL_SOURCES[path] + SHARED_SOURCES:
+        with open(os.path.join(_CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(workload: str):
+def recorded_traffic(workload: str, path: str = "gdn"):
     """Per-launch HBM bytes from rocprofv3 FETCH_SIZE / WRITE_SIZE runs, if
     they were taken on the current kernel source."""
     try:
@@ -54,7 +69,7 @@ def recorded_traffic(workload: str):
     except (OSError, ValueError):
         return None
     entry = rec.get(workload)
-    if not entry or entry.get("kernel_source_hash") != kernel_source_hash():
+    if not entry or entry.get("kernel_source_hash") != kernel_source_hash(path):
         return None
     return entry.get("bytes_per_launch")
 
@@ -92,14 +107,104 @@ def cpu_baseline(batch, n_seqs: int):
                       f"{dt:.2f} s incl. fp64 marshalling"}
 
 
+def conv_cpu_baseline(batch):
+    """The conv oracle, as it is, on the whole workload."""
+    import oracle
+
+    t0 = time.perf_counter()
+    oracle.conv_spec_update(batch.x, batch.weight, batch.bias, batch.cache, batch.cu_seqlens,
+                            batch.conv_indices, batch.num_accepted_tokens,
+                            token_indx=batch.token_indx, out_dtype=batch.out_dtype,
+                            activation=batch.activation)
+    dt = time.perf_counter() - t0
+    tokens = batch.draft_tokens()
+    return {"value": tokens / dt, "unit": "draft tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"all {batch.num_seqs} sequences ({tokens} draft tokens, "
+                      f"{batch.channels} channels) of the same workload; serial C, float64; "
+                      f"{dt:.2f} s incl. fp64 marshalling"}
+
+
+def time_steps(step, steps: int, warmup: int, stream):
+    """Warm up, then time ``steps`` back-to-back steps on ``stream``, twice.
+
+    In both passes the host enqueues every timed step while the GPU is held
+    busy by a spin kernel queued just before the timed region, so the GPU
+    runs the steps back to back whatever the per-call host cost.  Pass 1
+    brackets every launch with its own pair of HIP events (percentiles);
+    pass 2 records one pair around all of them, so the average launch
+    duration it gives carries no per-launch event overhead -- which matters
+    for a kernel of a few microseconds.  Returns (pass-2 GPU ms for all
+    steps, sorted pass-1 per-step ms, host wall seconds of pass 2).
+    """
+    import torch
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # host cost of one step (call + two event records), to size the spin
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    t = time.perf_counter()
+    for i in range(8):
+        e[0].record(stream)
+        step(i)
+        e[1].record(stream)
+    host_s = (time.perf_counter() - t) / 8
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    torch.cuda._sleep(1 << 20)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    cycles_per_ms = (1 << 20) / max(c0.elapsed_time(c1), 1e-3)
+    spin_cycles = int((2.0 * steps * host_s * 1e3 + 5.0) * cycles_per_ms)
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(spin_cycles)
+    for i, (e0, e1) in enumerate(ev):
+        e0.record(stream)
+        step(warmup + i)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    per_launch = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    torch.cuda._sleep(spin_cycles)
+    start.record(stream)
+    for i in range(steps):
+        step(warmup + steps + i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(end), per_launch, wall
+
+
+def timing_fields(gpu_ms, kern_ms, steps):
+    """Roofline timing fields: the average launch duration of pass 2 and
+    the per-launch event statistics of pass 1."""
+    n = len(kern_ms)
+    return {"kernel_avg_us": gpu_ms / steps * 1e3,
+            "event_pair_avg_us": sum(kern_ms) / n * 1e3,
+            "event_pair_median_us": kern_ms[n // 2] * 1e3,
+            "event_pair_p10_us": kern_ms[n // 10] * 1e3,
+            "event_pair_p90_us": kern_ms[(9 * n) // 10] * 1e3}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--layers", type=int, default=4,
-                    help="state pools cycled through, one per GDN layer")
+    ap.add_argument("--path", choices=["gdn", "conv"], default="gdn",
+                    help="gdn: the recurrent state update (default); conv: the conv update "
+                         "with rewind that precedes it")
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--layers", type=int, default=None,
+                    help="layers cycled through, each with its own state (default 4 for "
+                         "gdn, 32 for conv)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run --steps plain device copies of MIB "
                          "MiB each (reference kernel for scaling HBM byte counters)")
@@ -128,6 +233,10 @@ def main():
         print(json.dumps({"calibrate_copy_bytes": n, "copies": args.steps}), flush=True)
         return
     ops.load_library()
+    args.workload = args.workload or DEFAULT_WORKLOAD[args.path]
+    args.layers = args.layers or DEFAULT_LAYERS[args.path]
+    if args.path == "conv":
+        return bench_conv(args, dev)
     batch = workloads.make(args.workload)
     print(f"bench: {args.workload}: {workloads.DESCRIPTIONS[args.workload]}", file=sys.stderr,
           flush=True)
@@ -141,41 +250,26 @@ def main():
         kw["state"] = pools[i % len(pools)]
         ops.forward_core(**kw)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    stream = torch.cuda.current_stream(dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i, (e0, e1) in enumerate(ev):
-        e0.record(stream)
-        step(args.warmup + i)
-        e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kern_ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
-    avg_ms = sum(kern_ms) / len(kern_ms)
-    med_ms = kern_ms[len(kern_ms) // 2]
-    print(f"bench: kernel avg {avg_ms * 1e3:.1f} us, median {med_ms * 1e3:.1f} us, "
-          f"p10 {kern_ms[len(kern_ms) // 10] * 1e3:.1f} us, "
-          f"p90 {kern_ms[(9 * len(kern_ms)) // 10] * 1e3:.1f} us", file=sys.stderr, flush=True)
-
+    gpu_ms, kern_ms, wall = time_steps(step, args.steps, args.warmup,
+                                       torch.cuda.current_stream(dev))
+    tf = timing_fields(gpu_ms, kern_ms, args.steps)
+    print("bench: " + ", ".join(f"{k} {v:.1f}" for k, v in tf.items()), file=sys.stderr,
+          flush=True)
+    avg_ms = tf["kernel_avg_us"] * 1e-3
     achieved = alg_bytes / (avg_ms * 1e-3) / 1e9
-    traffic = recorded_traffic(args.workload)
-    ms_per_step = wall * 1e3 / args.steps
+    traffic = recorded_traffic(args.workload, "gdn")
+    ms_per_step = gpu_ms / args.steps
     cpu = cpu_baseline(batch, min(args.cpu_seqs, batch.num_seqs)) if args.cpu_seqs > 0 else None
     dtypes = {torch.float32: "f32", torch.bfloat16: "bf16", torch.float16: "f16"}
     line = {
         "metric": "draft tokens/sec and achieved HBM GB/s (% of peak), B=128 T=8 BF16 state",
-        "value": tokens * args.steps / wall,
+        "value": tokens * args.steps / (gpu_ms * 1e-3),
         "unit": "draft tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "host_wall_s": wall,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -188,9 +282,68 @@ def main():
                    "algorithmic_bytes_per_step": alg_bytes, "layers_cycled": len(pools),
                    "pool_bytes_per_layer": batch.pool.numel() * batch.pool.element_size()},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
-                     "kernel_avg_us": avg_ms * 1e3, "kernel_median_us": med_ms * 1e3},
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic, **tf},
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_conv(args, dev):
+    """The conv update with rewind at its full shape; one JSON line."""
+    import torch
+
+    from speculative_decode_amd import ops, workloads
+
+    batch = workloads.make_conv(args.workload)
+    print(f"bench: {args.workload}: {workloads.CONV_DESCRIPTIONS[args.workload]}",
+          file=sys.stderr, flush=True)
+    kw = ops.conv_batch_args(batch, dev)
+    layers = []
+    for i in range(args.layers):
+        lk = dict(kw)
+        if i:
+            lk["cache"] = kw["cache"].clone()
+            lk["x"] = kw["x"].clone()
+        lk["out"] = torch.zeros(batch.x.shape, dtype=batch.out_dtype, device=dev)
+        layers.append(lk)
+
+    def step(i):
+        ops.conv_spec_update(**layers[i % len(layers)])
+
+    gpu_ms, kern_ms, wall = time_steps(step, args.steps, args.warmup,
+                                       torch.cuda.current_stream(dev))
+    tf = timing_fields(gpu_ms, kern_ms, args.steps)
+    print("bench: " + ", ".join(f"{k} {v:.2f}" for k, v in tf.items()), file=sys.stderr,
+          flush=True)
+    avg_ms = tf["kernel_avg_us"] * 1e-3
+    tokens = batch.draft_tokens()
+    alg_bytes = batch.algorithmic_bytes()
+    achieved = alg_bytes / (avg_ms * 1e-3) / 1e9
+    dtypes = {torch.float32: "f32", torch.bfloat16: "bf16", torch.float16: "f16"}
+    line = {
+        "metric": "conv update with rewind: draft tokens/sec and achieved HBM GB/s "
+                  "(% of peak), B=128 T=8",
+        "value": tokens * args.steps / (gpu_ms * 1e-3),
+        "unit": "draft tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": gpu_ms / args.steps,
+        "host_wall_s": wall,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {workloads.CONV_DESCRIPTIONS[args.workload]}",
+                   "sequences": batch.num_seqs, "draft_tokens_per_step": tokens,
+                   "channels": batch.channels, "width": batch.width,
+                   "state_len": batch.state_len, "x_dtype": dtypes[batch.x.dtype],
+                   "algorithmic_bytes_per_step": alg_bytes, "layers_cycled": len(layers)},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS,
+                     "traffic": recorded_traffic(args.workload, "conv"), **tf},
+        "cpu_baseline": conv_cpu_baseline(batch) if args.cpu_seqs > 0 else None,
     }
     print(json.dumps(line), flush=True)
 

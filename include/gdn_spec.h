@@ -74,7 +74,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 #define GDN_MAX_DRAFT_TOKENS 8
 #define GDN_HEAD_DIM 128
 

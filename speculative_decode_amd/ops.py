@@ -11,7 +11,10 @@ The argument list follows the fused post-conv MTP decode op of vLLM PR #51674
 q/k/v split views, gates a/b, A_log, dt_bias, state indices, cu_seqlens,
 num_accepted_tokens, the state pool, output gate z, norm weight, out,
 scale = K**-0.5, norm_eps = 1e-5), with the speculative slot table of PR
-#46090 and the gather index of PR #51812.
+#46090 and the gather index of PR #51812.  The conv update that precedes it
+(``include/gdn_conv.h``) takes the packed projection, the depthwise conv
+weight and bias and the wide rolling conv buffer of PR #46090's speculative
+path, with the rewind keyed by num_accepted_tokens of PR #51674.
 """
 from __future__ import annotations
 
@@ -23,7 +26,7 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdn_spec.so")
-ABI_VERSION = 1
+ABI_VERSION = 2
 MAX_DRAFT_TOKENS = 8
 
 GDN_F32, GDN_F16, GDN_BF16 = 0, 1, 2
@@ -60,6 +63,26 @@ class GdnStatePool(ctypes.Structure):
                 ("reserved", ctypes.c_int32), ("num_slots", ctypes.c_int64)]
 
 
+class GdnConvLayer(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("x_stride_tok", ctypes.c_int64),
+                ("out", ctypes.c_void_p), ("out_stride_tok", ctypes.c_int64),
+                ("weight", ctypes.c_void_p), ("bias", ctypes.c_void_p),
+                ("x_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("channels", ctypes.c_int32), ("width", ctypes.c_int32),
+                ("activation", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("n_tok", ctypes.c_int64)]
+
+
+class GdnConvCache(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32),
+                ("state_len", ctypes.c_int32), ("num_lines", ctypes.c_int64),
+                ("stride_line", ctypes.c_int64), ("stride_pos", ctypes.c_int64),
+                ("stride_chan", ctypes.c_int64)]
+
+
+CONV_MAX_WIDTH = 4
+CONV_ACT = {None: 0, "none": 0, "silu": 1}
+
 _lib = None
 
 # Every symbol the header declares, with its ctypes signature.
@@ -76,6 +99,15 @@ SIGNATURES = {
     "gdn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "gdn_abi_version": (ctypes.c_int32, []),
     "gdn_abi_struct_sizes": (None, [ctypes.POINTER(ctypes.c_size_t)] * 3),
+    "gdn_conv_spec_update": (ctypes.c_int, [ctypes.POINTER(GdnConvLayer),
+                                            ctypes.POINTER(GdnConvCache), _VP, _I32, _I32,
+                                            _VP, _VP, _VP, _VP]),
+    "gdn_conv_decode_update": (ctypes.c_int, [ctypes.POINTER(GdnConvLayer),
+                                              ctypes.POINTER(GdnConvCache), _VP, _I32, _VP,
+                                              _VP]),
+    "gdn_validate_conv_indices_host": (ctypes.c_int, [_I64, _I32, _I32, _I64, _VP, _I32, _I32,
+                                                      _VP, _VP, _VP, _VP, _I32, _VP]),
+    "gdn_conv_abi_struct_sizes": (None, [ctypes.POINTER(ctypes.c_size_t)] * 2),
 }
 
 
@@ -98,6 +130,10 @@ def load_library():
     sizes = [ctypes.c_size_t() for _ in range(3)]
     lib.gdn_abi_struct_sizes(*[ctypes.byref(s) for s in sizes])
     want = [ctypes.sizeof(GdnView), ctypes.sizeof(GdnLayer), ctypes.sizeof(GdnStatePool)]
+    csizes = [ctypes.c_size_t() for _ in range(2)]
+    lib.gdn_conv_abi_struct_sizes(*[ctypes.byref(s) for s in csizes])
+    sizes += csizes
+    want += [ctypes.sizeof(GdnConvLayer), ctypes.sizeof(GdnConvCache)]
     if [s.value for s in sizes] != want:
         raise RuntimeError(f"struct layout mismatch: library {[s.value for s in sizes]}, "
                            f"binding {want}")
@@ -299,4 +335,124 @@ def batch_args(batch, device, *, state=None, out=None):
                 non_spec_state_indices=d(batch.state_indices),
                 non_spec_token_indx=d(batch.non_spec_token_indx),
                 out=out, scale=batch.scale, norm_eps=batch.norm_eps,
+                max_q_len=max(1, batch.T))
+
+
+# ---- conv update with rewind (include/gdn_conv.h) ---------------------------
+def make_conv_layer(x, weight, bias, out, *, activation="silu") -> GdnConvLayer:
+    """Describe the conv inputs ``x`` [n_tok, C], the depthwise ``weight``
+    [C, width] (or torch's [C, 1, width]), ``bias`` [C] or None and ``out``
+    [n_tok, C] as a gdn_conv_layer (no data is touched)."""
+    if weight.dim() == 3 and weight.shape[1] == 1:
+        weight = weight[:, 0, :]
+    if x.dim() != 2 or out.dim() != 2 or tuple(out.shape) != tuple(x.shape):
+        raise ValueError("x and out must both be [n_tok, channels]")
+    n_tok, C = x.shape
+    if weight.dim() != 2 or weight.shape[0] != C:
+        raise ValueError(f"weight must be [channels={C}, width]")
+    if weight.dtype != torch.float32 or not weight.is_contiguous():
+        raise ValueError("weight must be a contiguous float32 tensor")
+    if bias is not None and (bias.dtype != torch.float32 or not bias.is_contiguous()
+                             or tuple(bias.shape) != (C,)):
+        raise ValueError("bias must be a contiguous float32 [channels] tensor or None")
+    if x.dtype not in _DTYPE or out.dtype not in _DTYPE:
+        raise ValueError("x and out must be float32, float16 or bfloat16")
+    for name, t in (("weight", weight), ("bias", bias), ("out", out)):
+        if t is not None and t.device != x.device:
+            raise ValueError(f"{name} is on {t.device}, x on {x.device}")
+    if activation not in CONV_ACT:
+        raise ValueError(f"activation must be one of {sorted(k for k in CONV_ACT if k)}")
+    empty = x.numel() == 0
+    if not empty and (x.stride(-1) != 1 or out.stride(-1) != 1):
+        raise ValueError("x and out must have a contiguous channel dim")
+    return GdnConvLayer(
+        None if empty else x.data_ptr(), 0 if empty else x.stride(0),
+        None if empty else out.data_ptr(), C if empty else out.stride(0),
+        weight.data_ptr(), None if bias is None else bias.data_ptr(),
+        _DTYPE[x.dtype], _DTYPE[out.dtype], C, weight.shape[1], CONV_ACT[activation], 0, n_tok)
+
+
+def make_conv_cache(cache: torch.Tensor) -> GdnConvCache:
+    """A [num_lines, state_len, C] buffer with any strides (a channel-major
+    buffer is passed as ``buf.transpose(1, 2)``)."""
+    if cache.dim() != 3 or cache.dtype not in _DTYPE:
+        raise ValueError("conv cache must be a float32/float16/bfloat16 "
+                         "[num_lines, state_len, channels] tensor")
+    return GdnConvCache(cache.data_ptr(), _DTYPE[cache.dtype], cache.shape[1], cache.shape[0],
+                        cache.stride(0), cache.stride(1), cache.stride(2))
+
+
+def _conv_weight(weight):
+    return weight[:, 0, :] if weight.dim() == 3 and weight.shape[1] == 1 else weight
+
+
+def conv_spec_update(x, weight, bias, cache, cu_seqlens, conv_indices, num_accepted_tokens, *,
+                     token_indx=None, out=None, activation="silu",
+                     max_q_len=MAX_DRAFT_TOKENS):
+    """Speculative conv update of ``cache`` in place with rewind; returns
+    ``out`` (default zeros shaped like ``x``; only processed rows are written)."""
+    lib = load_library()
+    if out is None:
+        out = torch.zeros_like(x)
+    dev = x.device
+    layer = make_conv_layer(x, _conv_weight(weight), bias, out, activation=activation)
+    cc = make_conv_cache(cache)
+    cu = _meta(cu_seqlens, "cu_seqlens", dev)
+    li = _meta(conv_indices, "conv_indices", dev)
+    na = _meta(num_accepted_tokens, "num_accepted_tokens", dev)
+    ti = _meta(token_indx, "token_indx", dev)
+    B = cu.shape[0] - 1
+    if li.shape[0] != B or na.shape[0] != B:
+        raise ValueError("cu_seqlens, conv_indices, num_accepted_tokens disagree on B")
+    _check(lib.gdn_conv_spec_update(ctypes.byref(layer), ctypes.byref(cc), _ptr(cu), B,
+                                    int(max_q_len), _ptr(li), _ptr(na), _ptr(ti), _stream(dev)))
+    return out
+
+
+def conv_decode_update(x, weight, bias, cache, conv_indices, *, token_indx=None, out=None,
+                       activation="silu"):
+    """Non-speculative single-token conv update at line ``conv_indices[i]``
+    (negative = padding); returns ``out`` (default zeros)."""
+    lib = load_library()
+    if out is None:
+        out = torch.zeros_like(x)
+    dev = x.device
+    layer = make_conv_layer(x, _conv_weight(weight), bias, out, activation=activation)
+    cc = make_conv_cache(cache)
+    li = _meta(conv_indices, "conv_indices", dev)
+    ti = _meta(token_indx, "token_indx", dev)
+    _check(lib.gdn_conv_decode_update(ctypes.byref(layer), ctypes.byref(cc), _ptr(li),
+                                      li.shape[0], _ptr(ti), _stream(dev)))
+    return out
+
+
+def validate_conv_indices(num_lines: int, state_len: int, width: int, n_tok: int, *,
+                          cu_seqlens=None, conv_indices=None, num_accepted_tokens=None,
+                          spec_token_indx=None, decode_indices=None, decode_token_indx=None,
+                          max_q_len=MAX_DRAFT_TOKENS):
+    """Check the conv metadata contract on host copies
+    (gdn_validate_conv_indices_host).  Raises GdnError with the first violation."""
+    lib = load_library()
+
+    def host(t):
+        return None if t is None else t.detach().to("cpu", torch.int32).contiguous()
+
+    cu, li, na = host(cu_seqlens), host(conv_indices), host(num_accepted_tokens)
+    st, dl, dt = host(spec_token_indx), host(decode_indices), host(decode_token_indx)
+    B = 0 if cu is None else cu.shape[0] - 1
+    _check(lib.gdn_validate_conv_indices_host(
+        int(num_lines), int(state_len), int(width), int(n_tok), _ptr(cu), B, int(max_q_len),
+        _ptr(li), _ptr(na), _ptr(st), _ptr(dl), 0 if dl is None else dl.shape[0], _ptr(dt)))
+
+
+def conv_batch_args(batch, device, *, cache=None, out=None):
+    """Device copies of a workloads.ConvBatch as keyword arguments of
+    conv_spec_update (convenience for tests and the benchmark)."""
+    def d(t):
+        return None if t is None else t.to(device)
+    return dict(x=d(batch.x), weight=d(batch.weight), bias=d(batch.bias),
+                cache=d(batch.cache) if cache is None else cache,
+                cu_seqlens=d(batch.cu_seqlens), conv_indices=d(batch.conv_indices),
+                num_accepted_tokens=d(batch.num_accepted_tokens),
+                token_indx=d(batch.token_indx), out=out, activation=batch.activation,
                 max_q_len=max(1, batch.T))

@@ -1,0 +1,197 @@
+"""The conv-update C ABI on the CPU: struct layout, argument errors, no-op
+cases and the host metadata validator (no device call is made on any of
+these paths: CPU tensors stand in for device buffers, and every call here
+either returns before enqueueing or is rejected)."""
+import ctypes
+import os
+
+import pytest
+import torch
+
+from speculative_decode_amd import ops, workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ops.LIB_PATH):
+        import speculative_decode_amd.build as b
+        b.build()
+    return ops.load_library()
+
+
+def test_conv_struct_layout_and_width_limit(lib):
+    sizes = [ctypes.c_size_t() for _ in range(2)]
+    lib.gdn_conv_abi_struct_sizes(*[ctypes.byref(s) for s in sizes])
+    assert [s.value for s in sizes] == [ctypes.sizeof(ops.GdnConvLayer),
+                                        ctypes.sizeof(ops.GdnConvCache)]
+    hdr = open(os.path.join(ROOT, "include", "gdn_conv.h")).read()
+    assert f"#define GDN_CONV_MAX_WIDTH {ops.CONV_MAX_WIDTH}" in hdr
+
+
+def _layer_and_cache(C=16, W=4, n_tok=4, S=10, lines=4, dt=torch.bfloat16, out_dt=None):
+    x = torch.zeros(n_tok, C, dtype=dt)
+    out = torch.zeros(n_tok, C, dtype=out_dt or dt)
+    w = torch.zeros(C, W)
+    b = torch.zeros(C)
+    cache = torch.zeros(lines, S, C, dtype=dt)
+    keep = (x, out, w, b, cache)
+    return ops.make_conv_layer(x, w, b, out), ops.make_conv_cache(cache), keep
+
+
+def _spec(lib, layer, cache, *, B=1, max_q_len=8, meta=True):
+    m = torch.zeros(16, dtype=torch.int32)
+    p = ctypes.c_void_p(m.data_ptr()) if meta else None
+    return lib.gdn_conv_spec_update(ctypes.byref(layer), ctypes.byref(cache), p, B, max_q_len,
+                                    p, p, None, None)
+
+
+def test_empty_batches_are_no_ops(lib):
+    layer, cache, keep = _layer_and_cache()
+    assert _spec(lib, layer, cache, B=0) == 0
+    assert lib.gdn_conv_decode_update(ctypes.byref(layer), ctypes.byref(cache), None, 0, None,
+                                      None) == 0
+    x = torch.zeros(0, 16, dtype=torch.bfloat16)
+    empty = ops.make_conv_layer(x, torch.zeros(16, 4), None, torch.zeros_like(x))
+    assert _spec(lib, empty, cache, B=3) == 0
+
+
+@pytest.mark.parametrize("mutate,status,needle", [
+    (lambda L, C: setattr(L, "width", 5), 2, "exceeds"),
+    (lambda L, C: setattr(L, "width", 0), 1, "width"),
+    (lambda L, C: setattr(L, "channels", 0), 1, "channels"),
+    (lambda L, C: setattr(L, "x_dtype", 9), 2, "x_dtype"),
+    (lambda L, C: setattr(L, "out_dtype", -1), 2, "out_dtype"),
+    (lambda L, C: setattr(L, "activation", 2), 1, "activation"),
+    (lambda L, C: setattr(L, "weight", None), 1, "weight"),
+    (lambda L, C: setattr(L, "x", None), 1, "NULL"),
+    (lambda L, C: setattr(L, "out_stride_tok", 8), 1, "overlap"),
+    (lambda L, C: setattr(L, "x", L.x + 1), 1, "aligned"),
+    (lambda L, C: setattr(C, "dtype", 0), 2, "differs"),
+    (lambda L, C: setattr(C, "data", None), 1, "cache.data"),
+    (lambda L, C: setattr(C, "num_lines", 0), 1, "num_lines"),
+    (lambda L, C: setattr(C, "state_len", 2), 1, "state_len"),
+    (lambda L, C: setattr(C, "stride_pos", -1), 1, "strides"),
+])
+def test_argument_errors(lib, mutate, status, needle):
+    layer, cache, keep = _layer_and_cache()
+    mutate(layer, cache)
+    assert _spec(lib, layer, cache) == status
+    assert needle in ops.last_error(), ops.last_error()
+    assert lib.gdn_conv_decode_update(ctypes.byref(layer), ctypes.byref(cache), None, 1, None,
+                                      None) == status
+
+
+def test_spec_entry_errors(lib):
+    layer, cache, keep = _layer_and_cache(S=10)
+    assert _spec(lib, layer, cache, max_q_len=9) == 2 and "exceeds" in ops.last_error()
+    assert _spec(lib, layer, cache, max_q_len=0) == 1
+    assert _spec(lib, layer, cache, B=-1) == 1
+    assert _spec(lib, layer, cache, meta=False) == 1 and "NULL" in ops.last_error()
+    short, cache9, keep2 = _layer_and_cache(S=9)     # width - 2 + 8 = 10 > 9
+    assert _spec(lib, short, cache9, max_q_len=8) == 1 and "state_len" in ops.last_error()
+    assert lib.gdn_conv_decode_update(ctypes.byref(layer), ctypes.byref(cache), None, 2, None,
+                                      None) == 1
+    assert lib.gdn_conv_decode_update(ctypes.byref(layer), ctypes.byref(cache), None, -1, None,
+                                      None) == 1
+
+
+def test_binding_checks_shapes_on_host():
+    x = torch.zeros(4, 16)
+    with pytest.raises(ValueError):
+        ops.make_conv_layer(x, torch.zeros(8, 4), None, torch.zeros(4, 16))
+    with pytest.raises(ValueError):
+        ops.make_conv_layer(x, torch.zeros(16, 4), torch.zeros(8), torch.zeros(4, 16))
+    with pytest.raises(ValueError):
+        ops.make_conv_layer(x, torch.zeros(16, 4), None, torch.zeros(4, 16), activation="relu")
+    with pytest.raises(ValueError):
+        ops.make_conv_cache(torch.zeros(2, 3, 4, 5))
+    # torch's depthwise conv1d weight [C, 1, W] is accepted as is
+    L = ops.make_conv_layer(x, torch.zeros(16, 1, 4)[:, 0, :], None, torch.zeros(4, 16))
+    assert L.width == 4 and L.channels == 16
+    # a channel-major buffer passes as a transposed view
+    buf = torch.zeros(3, 16, 7)
+    cc = ops.make_conv_cache(buf.transpose(1, 2))
+    assert (cc.state_len, cc.stride_pos, cc.stride_chan) == (7, 1, 7)
+
+
+# -- metadata contract (host validator) ------------------------------------------
+def _validate(b, n_tok=None, **over):
+    args = dict(cu_seqlens=b.cu_seqlens, conv_indices=b.conv_indices,
+                num_accepted_tokens=b.num_accepted_tokens, spec_token_indx=b.token_indx,
+                max_q_len=b.T)
+    args.update(over)
+    ops.validate_conv_indices(b.cache.shape[0], b.state_len, b.width,
+                              b.n_tok if n_tok is None else n_tok, **args)
+
+
+def test_validator_accepts_generated_workloads(lib):
+    _validate(workloads.make_conv("conv_tiny"))
+    _validate(workloads.conv_batch(B=5, T=4, C=8, dtype="f32", num_lines=9, gather=True,
+                                   q_lens=[4, 0, 2, 1, 3], seed=1))
+    # decode entries with padding on lines no spec sequence uses
+    b = workloads.conv_batch(B=2, T=3, C=8, dtype="f32", num_lines=6, seed=2)
+    free = sorted(set(range(6)) - set(b.conv_indices.tolist()))
+    _validate(b, n_tok=b.n_tok + 3,
+              decode_indices=torch.tensor([free[0], -1, free[1]], dtype=torch.int32),
+              decode_token_indx=torch.tensor([b.n_tok, b.n_tok + 1, b.n_tok + 2],
+                                             dtype=torch.int32))
+
+
+@pytest.mark.parametrize("case,needle", [
+    ("acc_neg", "num_accepted"),
+    ("acc_high", "outside the line"),
+    ("line_range", "outside"),
+    ("dup_line", "used twice"),
+    ("row_range", "row"),
+    ("row_twice", "used twice"),
+    ("too_long", "max_q_len"),
+    ("short_buffer", "state_len"),
+    ("cu_decreasing", "decreases"),
+    ("cu_start", "cu_seqlens[0]"),
+    ("dec_dup_spec", "used twice"),
+])
+def test_validator_rejects(lib, case, needle):
+    b = workloads.conv_batch(B=3, T=3, C=8, dtype="f32", num_lines=6, gather=True, seed=4)
+    li, acc = b.conv_indices.clone(), b.num_accepted_tokens.clone()
+    cu, tix = b.cu_seqlens.clone(), b.token_indx.clone()
+    over = {}
+    if case == "acc_neg":
+        acc[0] = -1
+    elif case == "acc_high":
+        acc[1] = b.state_len - b.width + 3      # offset acc - 1 one past the last history
+    elif case == "line_range":
+        li[2] = 6
+    elif case == "dup_line":
+        li[1] = li[0]
+    elif case == "row_range":
+        tix[4] = b.n_tok
+    elif case == "row_twice":
+        tix[4] = tix[5]
+    elif case == "too_long":
+        over["max_q_len"] = 2
+    elif case == "short_buffer":
+        over = dict(max_q_len=3)
+        ops.validate_conv_indices(6, b.state_len, b.width, b.n_tok, cu_seqlens=cu,
+                                  conv_indices=li, num_accepted_tokens=acc,
+                                  spec_token_indx=tix, max_q_len=3)
+        with pytest.raises(ops.GdnError) as ei:
+            ops.validate_conv_indices(6, b.state_len - 1, b.width, b.n_tok, cu_seqlens=cu,
+                                      conv_indices=li, num_accepted_tokens=acc,
+                                      spec_token_indx=tix, max_q_len=3)
+        assert needle in ei.value.reason
+        return
+    elif case == "cu_decreasing":
+        cu[2] = cu[1] - 1
+    elif case == "cu_start":
+        cu = cu + 1
+    elif case == "dec_dup_spec":
+        over = dict(decode_indices=li[:1].clone(),
+                    decode_token_indx=torch.tensor([b.n_tok], dtype=torch.int32))
+    n_tok = b.n_tok + 1 if case == "dec_dup_spec" else b.n_tok
+    with pytest.raises(ops.GdnError) as ei:
+        ops.validate_conv_indices(6, b.state_len, b.width, n_tok, cu_seqlens=cu,
+                                  conv_indices=li, num_accepted_tokens=acc, spec_token_indx=tix,
+                                  **{"max_q_len": 3, **over})
+    assert needle in ei.value.reason, ei.value.reason
