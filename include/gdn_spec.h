@@ -74,7 +74,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 2
+#define GDN_ABI_VERSION 3
 #define GDN_MAX_DRAFT_TOKENS 8
 #define GDN_HEAD_DIM 128
 
@@ -167,6 +167,26 @@ gdn_status gdn_spec_decode_update(const gdn_layer* layer,
 gdn_status gdn_decode_update(const gdn_layer* layer, const gdn_state_pool* pool,
                              const int32_t* state_indices, int32_t num_tokens,
                              const int32_t* token_indx, hipStream_t stream);
+
+/*
+ * A mixed batch in ONE launch: the num_seqs speculative sequences of
+ * gdn_spec_decode_update (rows through spec_token_indx) and the num_tokens
+ * single-token entries of gdn_decode_update (slot state_indices[i], negative
+ * = padding, rows through non_spec_token_indx), one workgroup per (entry,
+ * value head) of either kind.  The result equals the two calls made one
+ * after the other, in either order; the two parts must touch disjoint slots
+ * and rows (gdn_validate_indices_host checks both parts together).  Either
+ * count may be 0.  The [51674] CUDA path gave this fusion up as low-gain
+ * (实现拆解, evolution notes: it needed prefix-length metadata and slicing);
+ * here the two index arrays already carry all it needs.
+ */
+gdn_status gdn_mixed_decode_update(const gdn_layer* layer, const gdn_state_pool* pool,
+                                   const int32_t* cu_seqlens, int32_t num_seqs,
+                                   int32_t max_q_len, const int32_t* spec_state_indices,
+                                   int32_t spec_stride, const int32_t* num_accepted_tokens,
+                                   const int32_t* spec_token_indx,
+                                   const int32_t* state_indices, int32_t num_tokens,
+                                   const int32_t* non_spec_token_indx, hipStream_t stream);
 
 /*
  * Host-side check of the metadata contract on HOST copies of the index

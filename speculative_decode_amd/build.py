@@ -28,6 +28,9 @@ def command(out: str) -> list:
     return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
             # packed-FP32 VALU forms are kept out of the generated code
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # fused multiply-adds only where the source writes fmaf: every
+            # instantiation then rounds the same expression the same way
+            "-ffp-contract=off",
             "-Wall", "-Wno-unused-command-line-argument",
             "-o", out] + SOURCES
 

@@ -76,7 +76,11 @@ struct KParams {
     const int32_t* num_acc;
     const int32_t* tix;
     const int32_t* state_idx;
+    const int32_t* ns_tix;    // gather of the single-token entries of a mixed launch
+    int64_t num_spec;         // sequences of the spec part
+    int64_t num_ns;           // single-token entries of a mixed launch (0: pure spec)
     int32_t spec_stride;
+    int32_t max_writes;       // host bound on slot writes per unit (launch planning only)
 };
 
 // ---- cross-lane sums -------------------------------------------------------
@@ -147,15 +151,32 @@ gdn_update_kernel(const KParams p)
     const int64_t xcd = blockIdx.x % NXCD;
     const int64_t per = nblk / NXCD, rem = nblk % NXCD;
     const int64_t unit = xcd * per + (xcd < rem ? xcd : rem) + blockIdx.x / NXCD;
-    const int64_t seq = unit / p.HV;
-    const int h = static_cast<int>(unit - seq * p.HV);
+    const int64_t entry = unit / p.HV;
+    const int h = static_cast<int>(unit - entry * p.HV);
     const int kh = h / p.group;
 
-    // ---- unit metadata (uniform), fetched in one batch ----
+    // A mixed launch interleaves its two kinds of entries in proportion, so
+    // that every XCD's contiguous range gets its share of the heavier spec
+    // units: entry e is spec sequence floor(e*S/E) when that count steps at
+    // e, else single-token entry e - floor(e*S/E) (S spec of E entries; a
+    // bijection).
+    bool spec_unit = SPEC;
+    int64_t seq = entry;
+    if (SPEC && p.num_ns > 0) {
+        const int64_t E = p.num_spec + p.num_ns;
+        const int64_t before = entry * p.num_spec / E;
+        const int64_t after = (entry + 1) * p.num_spec / E;
+        spec_unit = after > before;
+        seq = spec_unit ? before : entry - before;
+    }
+
+    // ---- unit metadata (uniform), fetched in one batch.  The single-token
+    // entries of a mixed launch read and write one slot in place. ----
     int L;
     int64_t c0, rslot;
     int64_t wslot[NT];
-    if constexpr (SPEC) {
+    const int32_t* tix = p.tix;
+    if (spec_unit) {
         c0 = p.cu[seq];
         L = static_cast<int>(p.cu[seq + 1] - c0);
         const int acc = p.num_acc[seq];
@@ -176,11 +197,15 @@ gdn_update_kernel(const KParams p)
         if (bad)
             return;
     } else {
-        rslot = p.state_idx[seq];
-        c0 = seq;
+        const int64_t i = seq;
+        tix = SPEC ? p.ns_tix : p.tix;
+        rslot = p.state_idx[i];
+        c0 = i;
         L = 1;
-        wslot[0] = rslot;
-        const int64_t row = p.tix ? p.tix[seq] : seq;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            wslot[t] = rslot;
+        const int64_t row = tix ? tix[i] : i;
         if (rslot < 0 || rslot >= p.num_slots || row < 0 || row >= p.n_tok)
             return;
     }
@@ -196,7 +221,7 @@ gdn_update_kernel(const KParams p)
     for (int i = 0; i < NTW; ++i) {
         const int t = wave + 4 * i;
         const int tt = t < L ? t : L - 1;
-        const int64_t row = p.tix ? p.tix[c0 + tt] : c0 + tt;
+        const int64_t row = tix ? tix[c0 + tt] : c0 + tt;
         rowv[i] = row;
         qr[i] = load_pair_raw<ACT>(p.q, row * p.q_st + kh * p.q_sh + 2 * lane);
         kr[i] = load_pair_raw<ACT>(p.k, row * p.k_st + kh * p.k_sh + 2 * lane);
@@ -411,27 +436,42 @@ constexpr size_t static_lds_bytes(int nt)
 // Blocks resident per CU before a batch counts as large.
 constexpr int ROUND_BLOCKS_PER_CU = 4;
 
-// Dynamic LDS to reserve for a launch of nunits blocks.  Each block writes up
-// to eight scattered state tiles for the one it reads.  With several such
-// blocks per CU, the write streams of the whole chip land on more DRAM rows
-// at once than the memory keeps open, and the sustained rate drops.  So once
-// a batch is larger than one round of resident blocks, the launch reserves
-// LDS that the kernel never touches -- just over half a CU's -- so that one
-// block runs per CU.  The stores of a finishing block still drain while the
-// CU's next block loads.  A smaller batch keeps every unit resident at once.
+// Concurrent blocks per CU for a large batch whose units write up to
+// `writes` state tiles each (0: no cap).  A unit reads one tile and writes up
+// to `writes`.  With many such write streams per CU, the chip's writes land
+// on more DRAM rows at once than the memory keeps open, and the sustained
+// rate drops: seven- and eight-token units run best one per CU, two- to
+// six-token units two per CU.  Single-token units read as much as they write
+// and need the concurrency to hide their read latency, so they run uncapped.
+int blocks_per_cu_for(int writes)
+{
+    if (writes <= 1)
+        return 0;
+    return writes <= 6 ? 2 : 1;
+}
+
+// Dynamic LDS to reserve for a launch of nunits blocks.  Once a batch is
+// larger than one round of resident blocks, the launch reserves LDS that the
+// kernel never touches -- just over 1/(n+1) of a CU's, counting the static
+// LDS -- so that at most n blocks run per CU (n from blocks_per_cu_for).  The
+// stores of a finishing block still drain while the CU's next block loads.
+// A smaller batch keeps every unit resident at once.
 template <int NT>
-hipError_t plan_lds(int64_t nunits, size_t* lds)
+hipError_t plan_lds(int64_t nunits, int writes, size_t* lds)
 {
     *lds = 0;
+    const int n = blocks_per_cu_for(writes);
+    if (n == 0)
+        return hipSuccess;
     DeviceInfo d;
     hipError_t e = device_info(&d);
     if (e != hipSuccess)
         return e;
     if (nunits <= static_cast<int64_t>(d.cus) * ROUND_BLOCKS_PER_CU)
         return hipSuccess;
-    const size_t half = static_cast<size_t>(d.lds_per_cu) / 2 + 1;
-    if (half + static_lds_bytes(NT) <= static_cast<size_t>(d.lds_per_block))
-        *lds = half;
+    const size_t share = static_cast<size_t>(d.lds_per_cu) / (n + 1) + 1;
+    if (share > static_lds_bytes(NT) && share <= static_cast<size_t>(d.lds_per_block))
+        *lds = share - static_lds_bytes(NT);
     return hipSuccess;
 }
 
@@ -439,7 +479,7 @@ template <int A, int S, int O, bool SPEC>
 hipError_t launch_typed(const KParams& p, int64_t grid, hipStream_t stream)
 {
     size_t lds = 0;
-    hipError_t e = plan_lds<SPEC ? MAXT : 1>(grid, &lds);
+    hipError_t e = plan_lds<SPEC ? MAXT : 1>(grid, p.max_writes, &lds);
     if (e != hipSuccess)
         return e;
     KParams args = p;
@@ -545,6 +585,59 @@ extern "C" gdn_status gdn_spec_decode_update(const gdn_layer* layer,
     p.num_acc = num_accepted_tokens;
     p.tix = token_indx;
     p.spec_stride = spec_stride;
+    p.num_spec = num_seqs;
+    p.max_writes = max_q_len;
+    return device_status(
+        launch<true>(layer->act_dtype, pool->dtype, layer->out_dtype, p, grid, stream));
+}
+
+extern "C" gdn_status gdn_mixed_decode_update(const gdn_layer* layer,
+                                              const gdn_state_pool* pool,
+                                              const int32_t* cu_seqlens, int32_t num_seqs,
+                                              int32_t max_q_len,
+                                              const int32_t* spec_state_indices,
+                                              int32_t spec_stride,
+                                              const int32_t* num_accepted_tokens,
+                                              const int32_t* spec_token_indx,
+                                              const int32_t* state_indices, int32_t num_tokens,
+                                              const int32_t* non_spec_token_indx,
+                                              hipStream_t stream)
+{
+    gdn::clear_error();
+    gdn_status st;
+    if ((st = gdn::check_layer(layer)) != GDN_OK || (st = gdn::check_pool(pool)) != GDN_OK)
+        return st;
+    if (num_seqs < 0 || num_tokens < 0)
+        return gdn::fail(GDN_ERR_INVALID, "num_seqs or num_tokens is negative");
+    if (max_q_len < 1)
+        return gdn::fail(GDN_ERR_INVALID, "max_q_len must be >= 1");
+    if (max_q_len > GDN_MAX_DRAFT_TOKENS)
+        return gdn::fail(GDN_ERR_UNSUPPORTED, "max_q_len %d exceeds %d draft tokens",
+                         max_q_len, GDN_MAX_DRAFT_TOKENS);
+    if (spec_stride < 1)
+        return gdn::fail(GDN_ERR_INVALID, "spec_stride must be >= 1");
+    if ((num_seqs == 0 && num_tokens == 0) || layer->n_tok == 0)
+        return GDN_OK;
+    if (num_seqs > 0 && (!cu_seqlens || !spec_state_indices || !num_accepted_tokens))
+        return gdn::fail(GDN_ERR_INVALID, "spec metadata pointer is NULL");
+    if (num_tokens > 0 && !state_indices)
+        return gdn::fail(GDN_ERR_INVALID, "state_indices is NULL");
+    const int64_t grid =
+        (static_cast<int64_t>(num_seqs) + num_tokens) * layer->num_v_heads;
+    if (grid > 0x7fffffffLL)
+        return gdn::fail(GDN_ERR_INVALID, "(num_seqs + num_tokens) * num_v_heads exceeds the "
+                                          "grid limit");
+    KParams p = make_params(layer, pool);
+    p.cu = cu_seqlens;
+    p.spec_idx = spec_state_indices;
+    p.num_acc = num_accepted_tokens;
+    p.tix = spec_token_indx;
+    p.spec_stride = spec_stride;
+    p.num_spec = num_seqs;
+    p.state_idx = state_indices;
+    p.ns_tix = non_spec_token_indx;
+    p.num_ns = num_tokens;
+    p.max_writes = num_seqs > 0 ? max_q_len : 1;
     return device_status(
         launch<true>(layer->act_dtype, pool->dtype, layer->out_dtype, p, grid, stream));
 }
@@ -570,6 +663,7 @@ extern "C" gdn_status gdn_decode_update(const gdn_layer* layer, const gdn_state_
     p.state_idx = state_indices;
     p.tix = token_indx;
     p.spec_stride = 1;
+    p.max_writes = 1;
     return device_status(
         launch<false>(layer->act_dtype, pool->dtype, layer->out_dtype, p, grid, stream));
 }

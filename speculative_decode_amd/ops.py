@@ -26,7 +26,7 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdn_spec.so")
-ABI_VERSION = 2
+ABI_VERSION = 3
 MAX_DRAFT_TOKENS = 8
 
 GDN_F32, GDN_F16, GDN_BF16 = 0, 1, 2
@@ -93,6 +93,9 @@ SIGNATURES = {
                                               _VP, _I32, _VP, _VP, _VP]),
     "gdn_decode_update": (ctypes.c_int, [ctypes.POINTER(GdnLayer),
                                          ctypes.POINTER(GdnStatePool), _VP, _I32, _VP, _VP]),
+    "gdn_mixed_decode_update": (ctypes.c_int, [ctypes.POINTER(GdnLayer),
+                                               ctypes.POINTER(GdnStatePool), _VP, _I32, _I32,
+                                               _VP, _I32, _VP, _VP, _VP, _I32, _VP, _VP]),
     "gdn_validate_indices_host": (ctypes.c_int, [_I64, _I64, _VP, _I32, _I32, _VP, _I32,
                                                  _VP, _VP, _VP, _I32, _VP]),
     "gdn_last_error": (ctypes.c_char_p, []),
@@ -273,27 +276,68 @@ def decode_update(q, k, v, z, a, b, A_log, dt_bias, norm_weight, state, state_in
     return out
 
 
+def mixed_decode_update(q, k, v, z, a, b, A_log, dt_bias, norm_weight, state, cu_seqlens,
+                        spec_state_indices, num_accepted_tokens, state_indices, *,
+                        spec_token_indx=None, non_spec_token_indx=None, out=None, scale=None,
+                        norm_eps=1e-5, max_q_len=MAX_DRAFT_TOKENS):
+    """A mixed batch -- speculative sequences and single-token entries -- in
+    one launch; returns ``out`` (default zeros)."""
+    lib = load_library()
+    if out is None:
+        out = torch.zeros_like(z)
+    dev = q.device
+    layer = make_layer(q, k, v, z, a, b, A_log, dt_bias, norm_weight, out,
+                       scale=scale, norm_eps=norm_eps)
+    pool = make_pool(state)
+    cu = _meta(cu_seqlens, "cu_seqlens", dev)
+    si = _meta(spec_state_indices, "spec_state_indices", dev)
+    na = _meta(num_accepted_tokens, "num_accepted_tokens", dev)
+    st = _meta(spec_token_indx, "spec_token_indx", dev)
+    ns = _meta(state_indices, "state_indices", dev)
+    nst = _meta(non_spec_token_indx, "non_spec_token_indx", dev)
+    if si.dim() != 2:
+        raise ValueError("spec_state_indices must be [num_seqs, spec_stride]")
+    B = cu.shape[0] - 1
+    if si.shape[0] != B or na.shape[0] != B:
+        raise ValueError("cu_seqlens, spec_state_indices, num_accepted_tokens disagree on B")
+    _check(lib.gdn_mixed_decode_update(ctypes.byref(layer), ctypes.byref(pool), _ptr(cu), B,
+                                       int(max_q_len), _ptr(si), si.shape[1], _ptr(na),
+                                       _ptr(st), _ptr(ns), ns.shape[0], _ptr(nst),
+                                       _stream(dev)))
+    return out
+
+
 def forward_core(q, k, v, z, a, b, A_log, dt_bias, norm_weight, state, *,
                  spec_cu_seqlens=None, spec_state_indices=None, num_accepted_tokens=None,
                  spec_token_indx=None, non_spec_state_indices=None,
                  non_spec_token_indx=None, out=None, scale=None, norm_eps=1e-5,
-                 max_q_len=MAX_DRAFT_TOKENS):
+                 max_q_len=MAX_DRAFT_TOKENS, single_launch=True):
     """Spec / non-spec split of one batch (vLLM PR #51812, ``_forward_core``).
 
     A pure speculative batch passes ``spec_token_indx=None`` and runs one
     launch with no gather.  A mixed batch gathers the spec rows (q/k/v/z *and*
-    the gates a/b, with the same index) inside the spec launch and the
-    non-spec rows inside the single-token launch; both write their own rows of
-    one ``out``.
+    the gates a/b, with the same index) and the non-spec rows inside the
+    kernel; with ``single_launch`` (the default) both parts run in one launch
+    (``gdn_mixed_decode_update``), otherwise as a spec launch followed by a
+    single-token launch.  Either way each part writes its own rows of one
+    ``out``.
     """
     if out is None:
         out = torch.zeros_like(z)
-    if spec_cu_seqlens is not None and spec_cu_seqlens.shape[0] > 1:
+    has_spec = spec_cu_seqlens is not None and spec_cu_seqlens.shape[0] > 1
+    has_ns = non_spec_state_indices is not None and non_spec_state_indices.shape[0] > 0
+    if single_launch and has_spec and has_ns:
+        return mixed_decode_update(q, k, v, z, a, b, A_log, dt_bias, norm_weight, state,
+                                   spec_cu_seqlens, spec_state_indices, num_accepted_tokens,
+                                   non_spec_state_indices, spec_token_indx=spec_token_indx,
+                                   non_spec_token_indx=non_spec_token_indx, out=out,
+                                   scale=scale, norm_eps=norm_eps, max_q_len=max_q_len)
+    if has_spec:
         spec_decode_update(q, k, v, z, a, b, A_log, dt_bias, norm_weight, state,
                            spec_cu_seqlens, spec_state_indices, num_accepted_tokens,
                            token_indx=spec_token_indx, out=out, scale=scale,
                            norm_eps=norm_eps, max_q_len=max_q_len)
-    if non_spec_state_indices is not None and non_spec_state_indices.shape[0] > 0:
+    if has_ns:
         decode_update(q, k, v, z, a, b, A_log, dt_bias, norm_weight, state,
                       non_spec_state_indices, token_indx=non_spec_token_indx, out=out,
                       scale=scale, norm_eps=norm_eps)

@@ -248,3 +248,19 @@ def test_validator_padding_and_identity(lib):
     ops.validate_indices(4, 3, state_indices=torch.tensor([0, -1, 2], dtype=torch.int32))
     with pytest.raises(ops.GdnError):
         ops.validate_indices(4, 3, state_indices=torch.tensor([0, 0, 2], dtype=torch.int32))
+
+
+def test_mixed_entry_errors_and_no_op(lib):
+    layer, pool, keep = _layer_and_pool()
+    m = torch.zeros(16, dtype=torch.int32)
+    p = ctypes.c_void_p(m.data_ptr())
+    f = lib.gdn_mixed_decode_update
+    args = lambda B, nt, meta=p, ns=p, mql=4: (ctypes.byref(layer), ctypes.byref(pool), meta, B,
+                                               mql, meta, 4, meta, None, ns, nt, None, None)
+    assert f(*args(0, 0, None, None)) == 0                  # nothing to do: no pointer read
+    assert f(*args(-1, 2)) == 1 and "negative" in ops.last_error()
+    assert f(*args(1, -1)) == 1
+    assert f(*args(1, 0, meta=None)) == 1 and "spec metadata" in ops.last_error()
+    assert f(*args(0, 2, ns=None)) == 1 and "state_indices" in ops.last_error()
+    assert f(*args(1, 1, mql=9)) == 2 and "exceeds" in ops.last_error()
+    assert f(*args(1, 1, mql=0)) == 1

@@ -415,3 +415,73 @@ def test_capped_launch_nonspec(dev):
     b.state_indices[7] = -1
     b.state_indices[31] = -1
     check_full(b, dev)
+
+
+# --------------------------------------------------------------------------
+# a mixed batch in one launch (gdn_mixed_decode_update) equals the spec
+# launch followed by the single-token launch, byte for byte
+# --------------------------------------------------------------------------
+def _two_ways(batch, dev):
+    res = []
+    for single in (True, False):
+        args = ops.batch_args(batch, dev)
+        args["state"] = batch.pool.to(dev).clone()
+        args["out"] = torch.zeros((batch.n_tok, batch.HV, batch.V), dtype=batch.out_dtype,
+                                  device=dev)
+        o = ops.forward_core(single_launch=single, **args)
+        torch.cuda.synchronize()
+        res.append((args["state"].cpu(), o.cpu()))
+    return res
+
+
+@pytest.mark.parametrize("state", ["bf16", "f32"])
+def test_mixed_single_launch_equals_two_launches(dev, state):
+    b = workloads.mixed_batch(n_non_spec=40, n_spec=24, T=6, HK=4, HV=32, act="bf16",
+                              state=state, acc_lo=0, acc_hi=6, seed=23)
+    b.state_indices[5] = -1                    # padding inside the single-token part
+    (p1, o1), (p2, o2) = _two_ways(b, dev)
+    assert torch.equal(p1, p2) and torch.equal(o1, o2)
+    check_full(b, dev)                         # and the oracle (single launch by default)
+
+
+def test_mixed_single_launch_full_size(dev):
+    b = workloads.make("mixed_b128")
+    (p1, o1), (p2, o2) = _two_ways(b, dev)
+    assert torch.equal(p1, p2) and torch.equal(o1, o2)
+
+
+def test_mixed_entry_with_one_part_empty(dev):
+    """Zero single-token entries reduce to the spec launch; zero sequences to
+    the single-token launch."""
+    b = workloads.mixed_batch(n_non_spec=9, n_spec=7, T=3, HK=2, HV=8, act="f32",
+                              state="f32", seed=24)
+    a = ops.batch_args(b, dev)
+    common = dict(q=a["q"], k=a["k"], v=a["v"], z=a["z"], a=a["a"], b=a["b"], A_log=a["A_log"],
+                  dt_bias=a["dt_bias"], norm_weight=a["norm_weight"])
+    empty = torch.zeros(0, dtype=torch.int32, device=dev)
+    st1 = b.pool.to(dev).clone()
+    o1 = ops.mixed_decode_update(state=st1, cu_seqlens=a["spec_cu_seqlens"],
+                                 spec_state_indices=a["spec_state_indices"],
+                                 num_accepted_tokens=a["num_accepted_tokens"],
+                                 state_indices=empty, spec_token_indx=a["spec_token_indx"],
+                                 max_q_len=3, **common)
+    st2 = b.pool.to(dev).clone()
+    o2 = ops.spec_decode_update(state=st2, cu_seqlens=a["spec_cu_seqlens"],
+                                spec_state_indices=a["spec_state_indices"],
+                                num_accepted_tokens=a["num_accepted_tokens"],
+                                token_indx=a["spec_token_indx"], max_q_len=3, **common)
+    torch.cuda.synchronize()
+    assert torch.equal(st1, st2) and torch.equal(o1, o2)
+    st3 = b.pool.to(dev).clone()
+    zero_cu = torch.zeros(1, dtype=torch.int32, device=dev)
+    o3 = ops.mixed_decode_update(state=st3, cu_seqlens=zero_cu,
+                                 spec_state_indices=torch.zeros((0, 3), dtype=torch.int32,
+                                                                device=dev),
+                                 num_accepted_tokens=empty,
+                                 state_indices=a["non_spec_state_indices"],
+                                 non_spec_token_indx=a["non_spec_token_indx"], **common)
+    st4 = b.pool.to(dev).clone()
+    o4 = ops.decode_update(state=st4, state_indices=a["non_spec_state_indices"],
+                           token_indx=a["non_spec_token_indx"], **common)
+    torch.cuda.synchronize()
+    assert torch.equal(st3, st4) and torch.equal(o3, o4)
