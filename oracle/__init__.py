@@ -61,6 +61,9 @@ def _load():
     lib.orc_decode_update.restype = ctypes.c_int
     lib.orc_decode_update.argtypes = common_head + [vp, i32, vp,
                                                     i32, i32, i32, i32, d, d]
+    lib.orc_prefill_update.restype = ctypes.c_int
+    lib.orc_prefill_update.argtypes = common_head + [vp, i32, vp, vp, vp, i32,
+                                                     i32, i32, i32, i32, d, d]
     lib.orc_conv_update.restype = ctypes.c_int
     lib.orc_conv_update.argtypes = [vp, vp, ctypes.c_int, vp, ctypes.c_int, i64, i32, i64,
                                     i32, i32, vp, vp, i32, vp, i32, vp, vp, vp]
@@ -152,6 +155,29 @@ def decode_update(q, k, v, z, a, b, A_log, dt_bias, norm_weight, pool,
         HK, HV, K, V, float(scale), float(norm_eps))
     if rc:
         raise ValueError(f"oracle decode_update: {_ERR.get(rc, rc)}")
+    return (torch.from_numpy(pool64).to(pool.dtype),
+            torch.from_numpy(out64).to(odt))
+
+
+def prefill_update(q, k, v, z, a, b, A_log, dt_bias, norm_weight, pool, cu_seqlens,
+                   state_indices, *, has_initial_state=None, token_indx=None, chunk_size=64,
+                   out=None, out_dtype=None, scale=None, norm_eps=1e-5):
+    """Chunked prefill: one slot per sequence, the state rounded to the pool
+    dtype after every chunk_size-th token and after the last; returns
+    ``(pool_after, out_after)`` as new tensors."""
+    arrs, out64, odt, pool64, (n_tok, HK, HV, K, V) = _prepare(
+        q, k, v, z, a, b, A_log, dt_bias, norm_weight, pool, out, out_dtype)
+    cu = _i32(cu_seqlens)
+    si = _i32(state_indices)
+    hi = _i32(has_initial_state)
+    ti = _i32(token_indx)
+    scale = K ** -0.5 if scale is None else scale
+    rc = _load().orc_prefill_update(
+        *[_p(x) for x in arrs], _p(out64), _FMT[odt], _p(pool64), _FMT[pool.dtype],
+        pool.shape[0], n_tok, _p(cu), cu.shape[0] - 1, _p(si), _p(hi), _p(ti),
+        int(chunk_size), HK, HV, K, V, float(scale), float(norm_eps))
+    if rc:
+        raise ValueError(f"oracle prefill_update: {_ERR.get(rc, rc)}")
     return (torch.from_numpy(pool64).to(pool.dtype),
             torch.from_numpy(out64).to(odt))
 

@@ -197,6 +197,8 @@ typedef struct {
  *   S <- S + d k^T                      rank-1 write
  *   o <- S q^                           read-out after the token's update
  *   pool[wslot, h] <- round(S)          every post-token state to its slot
+ *                                       (skipped for wslot < 0: the prefill
+ *                                       loop stores at chunk ends itself)
  *   out[row, h] <- round(RMSNorm(o) * w * silu(z))   gated RMSNorm over V
  * The carry S itself stays in double: rounding happens only in the store
  * ([52191] 实现拆解 4: only slot reads/writes go through the state type).
@@ -235,7 +237,7 @@ static void token_step(const layer_t *L, unit_scratch *w, int h, int64_t row,
         w->o[vv] = acc;
     }
 
-    {
+    if (wslot >= 0) {
         double *dst = L->pool + (wslot * L->HV + h) * (int64_t)V * K;
         for (i = 0; i < V * K; ++i)
             dst[i] = orc_round(L->state_fmt, w->S[i]);
@@ -398,6 +400,86 @@ int orc_decode_update(const double *q, const double *k, const double *v,
             memcpy(w.S, pool + (s * HV + h) * (int64_t)V * K,
                    sizeof(double) * (size_t)V * (size_t)K);
             token_step(&L, &w, h, row, s);
+        }
+    }
+    scratch_free(&w);
+    return ORC_OK;
+}
+
+/*
+ * Chunked prefill of B sequences, rows cu[b] .. cu[b+1]-1 (or
+ * token_indx[cu[b] + t]), one state slot per sequence, state_indices[b]
+ * (negative: skipped).  [52191] 实现拆解 3-4 and its test notes: the
+ * inter-chunk kernel expands the narrow state into an FP32 buffer, runs the
+ * chunk in FP32 and writes the buffer back to the slot at the chunk's end, so
+ * the state is rounded once per chunk; the reference recurrence it is tested
+ * against takes a state dtype and a write interval to reproduce exactly that.
+ * Reading: per (sequence, v-head)
+ *   S = has_initial_state[b] ? pool[s, h] : 0       (NULL: every sequence has one)
+ *   for t < L_b: token_step() without a slot store; then, after every
+ *     chunk_size-th token of the call and after its last token:
+ *     pool[s, h] <- round(S) and S <- that rounded value
+ * Token semantics, the gated-RMSNorm output and the GQA map are those of the
+ * decode step, so a chunk of one token is one decode call (pinned).
+ */
+int orc_prefill_update(const double *q, const double *k, const double *v,
+                       const double *z, const double *a, const double *b,
+                       const double *A_log, const double *dt_bias,
+                       const double *norm_weight, double *out, int out_fmt,
+                       double *pool, int state_fmt, int64_t num_slots,
+                       int64_t n_tok, const int32_t *cu_seqlens, int32_t B,
+                       const int32_t *state_indices,
+                       const int32_t *has_initial_state,
+                       const int32_t *token_indx, int32_t chunk_size,
+                       int32_t HK, int32_t HV, int32_t K, int32_t V,
+                       double scale, double norm_eps)
+{
+    layer_t L = {q, k, v, z, a, b, A_log, dt_bias, norm_weight, out, out_fmt,
+                 pool, state_fmt, num_slots, HK, HV, K, V, scale, norm_eps};
+    unit_scratch w;
+    int32_t bi;
+    int h;
+    int64_t t, i;
+
+    if (!layer_ok(&L) || !fmt_ok(out_fmt) || !fmt_ok(state_fmt) || B < 0 ||
+        chunk_size < 1 || (B > 0 && (!cu_seqlens || !state_indices)))
+        return ORC_BAD_ARG;
+    for (bi = 0; bi < B; ++bi) {
+        int64_t start = cu_seqlens[bi];
+        int64_t len = (int64_t)cu_seqlens[bi + 1] - start;
+        if (len <= 0 || state_indices[bi] < 0)
+            continue;
+        if (start < 0 || state_indices[bi] >= num_slots)
+            return ORC_BAD_INDEX;
+        for (t = 0; t < len; ++t) {
+            int64_t row = token_indx ? token_indx[start + t] : start + t;
+            if (row < 0 || row >= n_tok)
+                return ORC_BAD_INDEX;
+        }
+    }
+    if (!scratch_alloc(&w, K, V)) {
+        scratch_free(&w);
+        return ORC_NO_MEMORY;
+    }
+    for (bi = 0; bi < B; ++bi) {
+        int64_t start = cu_seqlens[bi];
+        int64_t len = (int64_t)cu_seqlens[bi + 1] - start;
+        int64_t s = state_indices[bi];
+        if (len <= 0 || s < 0)
+            continue;
+        for (h = 0; h < HV; ++h) {
+            double *slot = pool + (s * HV + h) * (int64_t)V * K;
+            if (!has_initial_state || has_initial_state[bi])
+                memcpy(w.S, slot, sizeof(double) * (size_t)V * (size_t)K);
+            else
+                memset(w.S, 0, sizeof(double) * (size_t)V * (size_t)K);
+            for (t = 0; t < len; ++t) {
+                int64_t row = token_indx ? token_indx[start + t] : start + t;
+                token_step(&L, &w, h, row, -1);
+                if ((t + 1) % chunk_size == 0 || t == len - 1)
+                    for (i = 0; i < (int64_t)V * K; ++i)
+                        slot[i] = w.S[i] = orc_round(state_fmt, w.S[i]);
+            }
         }
     }
     scratch_free(&w);

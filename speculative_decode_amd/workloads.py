@@ -239,6 +239,136 @@ DESCRIPTIONS = {
 
 
 @dataclass
+class PrefillBatch:
+    """Chunked-prefill inputs (CPU tensors): B sequences of any length, rows
+    contiguous in sequence order, one state slot per sequence."""
+    name: str
+    HK: int
+    HV: int
+    K: int
+    V: int
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    z: torch.Tensor
+    a: torch.Tensor
+    b: torch.Tensor
+    A_log: torch.Tensor
+    dt_bias: torch.Tensor
+    norm_weight: torch.Tensor
+    pool: torch.Tensor
+    out_dtype: torch.dtype
+    cu_seqlens: torch.Tensor              # int32 [B+1]
+    state_indices: torch.Tensor           # int32 [B]
+    has_initial_state: Optional[torch.Tensor] = None   # int32 [B] or None (all)
+    token_indx: Optional[torch.Tensor] = None
+    chunk_size: int = 64
+    scale: float = 0.0
+    norm_eps: float = 1e-5
+
+    @property
+    def n_tok(self) -> int:
+        return self.q.shape[0]
+
+    @property
+    def num_seqs(self) -> int:
+        return self.cu_seqlens.shape[0] - 1
+
+    def tokens(self) -> int:
+        return int(self.cu_seqlens[-1])
+
+    def head_tokens(self) -> int:
+        return self.tokens() * self.HV
+
+    def algorithmic_bytes(self) -> int:
+        """Per sequence and v-head with a slot: the state read once (when it
+        has an initial state) and written once; per processed row: q, k per
+        key head, v, z, out per value head and the two gates; plus metadata
+        and parameters."""
+        s_state = self.pool.element_size()
+        s_act = self.q.element_size()
+        s_out = torch.empty((), dtype=self.out_dtype).element_size()
+        tile = self.HV * self.K * self.V * s_state
+        lens = (self.cu_seqlens[1:] - self.cu_seqlens[:-1]).clamp(min=0)
+        live = (lens > 0) & (self.state_indices >= 0)
+        init = live.clone()
+        if self.has_initial_state is not None:
+            init &= self.has_initial_state != 0
+        state = (int(live.sum()) + int(init.sum())) * tile
+        rows = int((lens * live).sum())
+        per_row = (2 * self.HK * self.K * s_act + self.HV * self.V * (2 * s_act + s_out)
+                   + 2 * self.HV * s_act)
+        meta = 4 * (self.cu_seqlens.numel() + self.state_indices.numel())
+        if self.has_initial_state is not None:
+            meta += 4 * self.has_initial_state.numel()
+        return state + rows * per_row + meta + 4 * (2 * self.HV + self.V)
+
+    def flops(self) -> int:
+        """Arithmetic of the recurrence: per processed (row, v-head), the
+        decay (K*V multiplies), S.k^ and S.q^ (2*K*V multiply-adds) and the
+        rank-1 update (K*V multiply-adds): 7*K*V flop."""
+        lens = (self.cu_seqlens[1:] - self.cu_seqlens[:-1]).clamp(min=0)
+        live = (lens > 0) & (self.state_indices >= 0)
+        return int((lens * live).sum()) * self.HV * 7 * self.K * self.V
+
+
+def prefill_batch(*, lens, HK, HV, K=128, V=128, act="bf16", state="bf16", out=None,
+                  num_slots=None, pool_std=0.05, chunk_size=64, init_frac=1.0, seed=0,
+                  name="prefill") -> PrefillBatch:
+    """Sequences of the given lengths, rows contiguous in order; slot of
+    sequence b from a permutation of the pool; has_initial_state ~
+    Bernoulli(init_frac) (None when init_frac is 1).  Draw order as for the
+    decode batches (q, k, v, z, a, b, A_log, dt_bias, norm_weight, the pool
+    slot by slot, the slot permutation), then has_initial_state."""
+    lens = np.asarray(lens, dtype=np.int64)
+    B = lens.shape[0]
+    num_slots = B if num_slots is None else num_slots
+    assert num_slots >= B
+    cu = np.zeros(B + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(np.maximum(lens, 0))
+    rng = np.random.Generator(np.random.PCG64(seed))
+    act_t, state_t = _DT[act], _DT[state]
+    q, k, v, z, a, b, A_log, dt_bias, w, pool = _common(
+        rng, int(cu[-1]), HK, HV, K, V, act_t, num_slots, pool_std, state_t)
+    perm = rng.permutation(num_slots).astype(np.int32)
+    hi = None
+    if init_frac < 1.0:
+        hi = torch.from_numpy((rng.random(B) < init_frac).astype(np.int32))
+    return PrefillBatch(name=name, HK=HK, HV=HV, K=K, V=V, q=q, k=k, v=v, z=z, a=a, b=b,
+                        A_log=A_log, dt_bias=dt_bias, norm_weight=w, pool=pool,
+                        out_dtype=_DT[out or act], cu_seqlens=torch.from_numpy(cu),
+                        state_indices=torch.from_numpy(perm[:B].copy()),
+                        has_initial_state=hi, chunk_size=chunk_size, scale=K ** -0.5)
+
+
+# Prefill workloads.  "prefill_b16_l2048": 16 sequences of 2048 tokens on the
+# layer shape of the decode workloads, BF16 state rounded every 64 tokens.
+PREFILL_CONFIGS = {
+    "prefill_small": dict(lens=[200, 77, 0, 131], HK=2, HV=8, act="bf16", state="bf16",
+                          chunk_size=32, init_frac=0.6, num_slots=6, seed=30),
+    "prefill_b16_l2048": dict(lens=[2048] * 16, HK=4, HV=32, act="bf16", state="bf16",
+                              chunk_size=64, seed=31),
+    "prefill_ragged_b32": dict(lens=[64 * (1 + (7 * i) % 24) for i in range(32)], HK=4, HV=32,
+                               act="bf16", state="bf16", chunk_size=64, init_frac=0.5, seed=32),
+}
+
+PREFILL_DESCRIPTIONS = {
+    "prefill_small": "prefill B=4 (200, 77, 0, 131 tokens) HK=2 HV=8 K=V=128, bf16, BF16 "
+                     "state, chunk 32",
+    "prefill_b16_l2048": "prefill B=16 x 2048 tokens HK=4 HV=32 K=V=128, bf16 activations, "
+                         "BF16 state rounded every 64 tokens",
+    "prefill_ragged_b32": "prefill B=32, 64..1536 tokens, HK=4 HV=32 K=V=128, bf16, BF16 "
+                          "state, chunk 64, half with an initial state",
+}
+
+
+def make_prefill(name: str, **overrides) -> PrefillBatch:
+    cfg = dict(PREFILL_CONFIGS[name])
+    cfg.update(overrides)
+    return prefill_batch(name=name, **cfg)
+
+
+@dataclass
 class ConvBatch:
     """Inputs of the conv update that precedes the recurrent update (CPU
     tensors).  ``x`` holds the conv inputs (the packed q/k/v projection before
