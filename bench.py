@@ -40,13 +40,16 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, AMD's published figure
-DEFAULT_WORKLOAD = {"gdn": "mtp_b128_bf16", "conv": "conv_mtp_b128"}
-DEFAULT_LAYERS = {"gdn": 4, "conv": 32}
+PEAK_FP32_TFLOPS = 157.3       # MI355X FP32 vector, AMD's published figure
+DEFAULT_WORKLOAD = {"gdn": "mtp_b128_bf16", "conv": "conv_mtp_b128",
+                    "prefill": "prefill_b16_l2048"}
+DEFAULT_LAYERS = {"gdn": 4, "conv": 32, "prefill": 2}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 _CSRC = os.path.join(ROOT, "speculative_decode_amd", "csrc")
 KERNEL_SOURCES = {
-    "gdn": ["gdn_kernels.hip", "gdn_host.cpp"],
+    "gdn": ["gdn_kernels.hip", "gdn_host.cpp", "lane_ops.h"],
     "conv": ["conv_kernels.hip", "conv_host.cpp"],
+    "prefill": ["prefill_kernels.hip", "gdn_host.cpp", "lane_ops.h"],
 }
 SHARED_SOURCES = ["gdn_internal.h", "dtype_cvt.h"]
 
@@ -198,9 +201,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--path", choices=["gdn", "conv"], default="gdn",
+    ap.add_argument("--path", choices=["gdn", "conv", "prefill"], default="gdn",
                     help="gdn: the recurrent state update (default); conv: the conv update "
-                         "with rewind that precedes it")
+                         "with rewind that precedes it; prefill: the chunked prefill")
     ap.add_argument("--workload", default=None)
     ap.add_argument("--layers", type=int, default=None,
                     help="layers cycled through, each with its own state (default 4 for "
@@ -237,6 +240,8 @@ def main():
     args.layers = args.layers or DEFAULT_LAYERS[args.path]
     if args.path == "conv":
         return bench_conv(args, dev)
+    if args.path == "prefill":
+        return bench_prefill(args, dev)
     batch = workloads.make(args.workload)
     print(f"bench: {args.workload}: {workloads.DESCRIPTIONS[args.workload]}", file=sys.stderr,
           flush=True)
@@ -344,6 +349,92 @@ def bench_conv(args, dev):
                      "frac": achieved / PEAK_HBM_GBS,
                      "traffic": recorded_traffic(args.workload, "conv"), **tf},
         "cpu_baseline": conv_cpu_baseline(batch) if args.cpu_seqs > 0 else None,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def prefill_cpu_baseline(batch):
+    """The prefill oracle, as it is, on the first sequence of the workload
+    (every head): a bounded sample of the same work."""
+    import torch
+
+    import oracle
+
+    L0 = int(batch.cu_seqlens[1])
+    t0 = time.perf_counter()
+    oracle.prefill_update(batch.q[:L0], batch.k[:L0], batch.v[:L0], batch.z[:L0],
+                          batch.a[:L0], batch.b[:L0], batch.A_log, batch.dt_bias,
+                          batch.norm_weight, batch.pool, batch.cu_seqlens[:2],
+                          batch.state_indices[:1],
+                          has_initial_state=None if batch.has_initial_state is None
+                          else batch.has_initial_state[:1],
+                          chunk_size=batch.chunk_size, out_dtype=batch.out_dtype)
+    dt = time.perf_counter() - t0
+    return {"value": L0 / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"the first of {batch.num_seqs} sequences ({L0} tokens, all "
+                      f"{batch.HV} v-heads) of the same workload; serial C, float64; "
+                      f"{dt:.2f} s incl. fp64 marshalling"}
+
+
+def bench_prefill(args, dev):
+    """The chunked prefill at its full shape; one JSON line.  Bound by the
+    FP32 vector ALU: the roofline is flops against the FP32 peak."""
+    import torch
+
+    from speculative_decode_amd import ops, workloads
+
+    batch = workloads.make_prefill(args.workload)
+    print(f"bench: {args.workload}: {workloads.PREFILL_DESCRIPTIONS[args.workload]}",
+          file=sys.stderr, flush=True)
+    kw = ops.prefill_batch_args(batch, dev)
+    layers = []
+    for i in range(args.layers):
+        lk = dict(kw)
+        if i:
+            for name in ("q", "k", "v", "z", "a", "b", "state"):
+                lk[name] = kw[name].clone()
+        lk["out"] = torch.zeros((batch.n_tok, batch.HV, batch.V), dtype=batch.out_dtype,
+                                device=dev)
+        layers.append(lk)
+
+    def step(i):
+        ops.prefill_update(**layers[i % len(layers)])
+
+    gpu_ms, kern_ms, wall = time_steps(step, args.steps, args.warmup,
+                                       torch.cuda.current_stream(dev))
+    tf = timing_fields(gpu_ms, kern_ms, args.steps)
+    print("bench: " + ", ".join(f"{k} {v:.1f}" for k, v in tf.items()), file=sys.stderr,
+          flush=True)
+    avg_s = tf["kernel_avg_us"] * 1e-6
+    flops = batch.flops()
+    tokens = batch.tokens()
+    achieved = flops / avg_s / 1e12
+    line = {
+        "metric": "chunked prefill: tokens/sec and achieved FP32 TFLOP/s (% of peak)",
+        "value": tokens * args.steps / (gpu_ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": gpu_ms / args.steps,
+        "host_wall_s": wall,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: "
+                               f"{workloads.PREFILL_DESCRIPTIONS[args.workload]}",
+                   "sequences": batch.num_seqs, "tokens_per_step": tokens,
+                   "HK": batch.HK, "HV": batch.HV, "chunk_size": batch.chunk_size,
+                   "flops_per_step": flops,
+                   "algorithmic_bytes_per_step": batch.algorithmic_bytes(),
+                   "achieved_hbm_gbs": batch.algorithmic_bytes() / avg_s / 1e9,
+                   "layers_cycled": len(layers)},
+        "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_TFLOPS,
+                     "traffic": recorded_traffic(args.workload, "prefill"), **tf},
+        "cpu_baseline": prefill_cpu_baseline(batch) if args.cpu_seqs > 0 else None,
     }
     print(json.dumps(line), flush=True)
 

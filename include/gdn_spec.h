@@ -74,7 +74,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 3
+#define GDN_ABI_VERSION 4
 #define GDN_MAX_DRAFT_TOKENS 8
 #define GDN_HEAD_DIM 128
 
@@ -187,6 +187,35 @@ gdn_status gdn_mixed_decode_update(const gdn_layer* layer, const gdn_state_pool*
                                    const int32_t* spec_token_indx,
                                    const int32_t* state_indices, int32_t num_tokens,
                                    const int32_t* non_spec_token_indx, hipStream_t stream);
+
+/*
+ * Chunked prefill ([52191] 实现拆解 items 3-4): num_seqs sequences of any
+ * length, rows cu_seqlens[b] .. cu_seqlens[b+1]-1 (through token_indx when
+ * given), sequence b on slot state_indices[b] (negative: skipped), read at
+ * the start when has_initial_state[b] != 0 (NULL: always; 0: start from a
+ * zero state) and written at the end.  Every row runs the token step above
+ * (same gates, norms, recurrence and gated-RMSNorm output); the carried
+ * state is rounded to the pool dtype after every chunk_size-th row of the
+ * call and after its last -- where the chunked kernels of the pages write
+ * the state back -- and continues from the rounded value.  A call split at
+ * a multiple of chunk_size therefore equals one call.  Slots distinct per
+ * call (gdn_validate_prefill_indices_host checks it).
+ */
+gdn_status gdn_prefill_update(const gdn_layer* layer, const gdn_state_pool* pool,
+                              const int32_t* cu_seqlens, int32_t num_seqs,
+                              const int32_t* state_indices,
+                              const int32_t* has_initial_state, const int32_t* token_indx,
+                              int32_t chunk_size, hipStream_t stream);
+
+/*
+ * Host-side check of prefill metadata on HOST copies: cu_seqlens
+ * non-decreasing from 0, slots < num_slots (negative = skipped) and
+ * distinct, rows inside [0, n_tok) and used once.
+ */
+gdn_status gdn_validate_prefill_indices_host(int64_t num_slots, int64_t n_tok,
+                                             const int32_t* cu_seqlens, int32_t num_seqs,
+                                             const int32_t* state_indices,
+                                             const int32_t* token_indx);
 
 /*
  * Host-side check of the metadata contract on HOST copies of the index

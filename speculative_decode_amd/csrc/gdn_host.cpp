@@ -246,3 +246,47 @@ extern "C" gdn_status gdn_validate_indices_host(
     }
     return GDN_OK;
 }
+
+extern "C" gdn_status gdn_validate_prefill_indices_host(int64_t num_slots, int64_t n_tok,
+                                                        const int32_t* cu, int32_t num_seqs,
+                                                        const int32_t* state_idx,
+                                                        const int32_t* tix)
+{
+    gdn::clear_error();
+    if (num_seqs < 0 || num_slots <= 0 || n_tok < 0)
+        return fail(GDN_ERR_INVALID, "negative count or empty pool");
+    if (num_seqs == 0)
+        return GDN_OK;
+    if (!cu || !state_idx)
+        return fail(GDN_ERR_INVALID, "cu_seqlens or state_indices is NULL");
+    if (cu[0] != 0)
+        return fail(GDN_ERR_INVALID, "cu_seqlens[0] = %d, expected 0", cu[0]);
+    std::vector<char> slot_used(static_cast<size_t>(num_slots), 0);
+    std::vector<char> row_used(static_cast<size_t>(n_tok), 0);
+    for (int32_t b = 0; b < num_seqs; ++b) {
+        const int64_t len = static_cast<int64_t>(cu[b + 1]) - cu[b];
+        if (len < 0)
+            return fail(GDN_ERR_INVALID, "cu_seqlens decreases at sequence %d", b);
+        const int64_t s = state_idx[b];
+        if (len == 0 || s < 0)
+            continue;
+        if (s >= num_slots)
+            return fail(GDN_ERR_INVALID, "sequence %d: slot %lld outside [0, %lld)", b,
+                        (long long)s, (long long)num_slots);
+        if (slot_used[s])
+            return fail(GDN_ERR_INVALID, "slot %lld is used by two sequences", (long long)s);
+        slot_used[s] = 1;
+        for (int64_t t = 0; t < len; ++t) {
+            const int64_t g = static_cast<int64_t>(cu[b]) + t;
+            const int64_t row = tix ? tix[g] : g;
+            if (row < 0 || row >= n_tok)
+                return fail(GDN_ERR_INVALID, "sequence %d: row %lld outside [0, %lld)", b,
+                            (long long)row, (long long)n_tok);
+            if (row_used[row])
+                return fail(GDN_ERR_INVALID, "sequence %d: row %lld used twice", b,
+                            (long long)row);
+            row_used[row] = 1;
+        }
+    }
+    return GDN_OK;
+}

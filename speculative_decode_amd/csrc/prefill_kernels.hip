@@ -1,0 +1,422 @@
+// prefill_kernels.hip -- chunked Gated DeltaNet prefill for CDNA4 (gfx950):
+// the recurrence of the speculative-decode update run over whole prompts,
+// one state slot per sequence, and its C-ABI entry point.
+//
+// What is computed is fixed by the vLLM PR reports on prhub.com.cn: the token
+// step of the decode update (#51674 实现拆解 item 1, #46090 fla.cpp excerpt),
+// and the chunk semantics of #52191 (实现拆解 items 3-4): FP32 arithmetic
+// throughout, the state rounded to its storage dtype once per chunk, when the
+// chunk's state is written back.  gdn_spec.h spells out the formula.
+//
+// How it is computed here:
+//   * One 256-thread workgroup per (sequence, value head), the 128 x 128
+//     state in registers exactly as in the decode kernel (each 8-lane group
+//     owns a row at a time, each lane 16 elements of 4 rows).  The state is
+//     read once, rounded in registers at every chunk end, and written once:
+//     intermediate chunk write-backs go to the same slot and are overwritten,
+//     so only the rounding is kept, not the stores.
+//   * Tokens are taken 8 at a time.  The normalised q/k, v, z, the gates and
+//     k^.q^ of a step are staged in LDS (double-buffered), and the next
+//     step's activation loads are issued before this step's token loop, so
+//     their latency hides behind the recurrence.
+//   * Why not the chunkwise (WY / UT-transform) form: it trades the serial
+//     recurrence for dense C x C, C x K and K x V products per chunk -- more
+//     arithmetic in total -- to run them on matrix cores.  On MI355X the
+//     FP32 matrix rate equals the FP32 vector rate, and the pages fix FP32
+//     arithmetic, so the chunkwise form would do more work at the same peak.
+//   * Prefill is compute-bound (about 130 flop per byte of HBM traffic): the
+//     roofline is the FP32 vector ALU.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "dtype_cvt.h"
+#include "gdn_internal.h"
+#include "lane_ops.h"
+
+namespace {
+
+using namespace gdn_dev;
+
+constexpr int D = GDN_HEAD_DIM;
+constexpr int NTHREADS = 256;
+constexpr int ROWS_PER_WAVE = D / (NTHREADS / 64);   // 32
+constexpr int RPT = ROWS_PER_WAVE / 8;               // rows per thread: 4
+constexpr int NE = D / 8;                            // elements per (thread, row): 16
+constexpr int NXCD = 8;
+constexpr int TS = 8;                                // tokens per step
+constexpr int NTW = TS / 4;                          // tokens per wave per step
+
+struct PParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* z;
+    const void* a;
+    const void* b;
+    void* out;
+    int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh, z_st, z_sh, a_st, b_st, o_st, o_sh;
+    const float* A_log;
+    const float* dt_bias;
+    const float* norm_weight;
+    void* pool;
+    int64_t num_slots;
+    int64_t n_tok;
+    int32_t HV;
+    int32_t group;
+    float scale;
+    float norm_eps;
+    const int32_t* cu;
+    const int32_t* state_idx;
+    const int32_t* has_init;
+    const int32_t* tix;
+    int32_t chunk;
+};
+
+// One step's staging: normalised k and q, v, z, the read-outs o, the gate
+// scalars and the rows of its 8 tokens.
+struct Step {
+    float k[TS][D];
+    float q[TS][D];
+    float v[TS][D];
+    float o[TS][D];
+    float z[TS][D];
+    float alpha[TS], beta[TS], kq[TS];
+    int64_t row[TS];
+};
+
+// The raw activations of one step for one wave (tokens wave, wave + 4).
+template <int ACT>
+struct StepRaw {
+    typename Pair<ACT>::raw q[NTW], k[NTW], v[NTW], z[NTW];
+    uint32_t a[NTW], b[NTW];
+    int64_t row[NTW];
+};
+
+template <int ACT>
+__device__ __forceinline__ void issue_step(const PParams& p, int64_t c0, int L, int step,
+                                           int wave, int lane, int h, int kh, StepRaw<ACT>& r)
+{
+#pragma unroll
+    for (int i = 0; i < NTW; ++i) {
+        const int t = step * TS + wave + 4 * i;
+        const int tt = t < L ? t : L - 1;        // clamped: always a valid row
+        const int64_t row = p.tix ? static_cast<int64_t>(p.tix[c0 + tt]) : c0 + tt;
+        r.row[i] = row;
+        r.q[i] = load_pair_raw<ACT>(p.q, row * p.q_st + kh * p.q_sh + 2 * lane);
+        r.k[i] = load_pair_raw<ACT>(p.k, row * p.k_st + kh * p.k_sh + 2 * lane);
+        r.v[i] = load_pair_raw<ACT>(p.v, row * p.v_st + h * p.v_sh + 2 * lane);
+        r.z[i] = load_pair_raw<ACT>(p.z, row * p.z_st + h * p.z_sh + 2 * lane);
+        r.a[i] = load_one_raw<ACT>(p.a, row * p.a_st + h);
+        r.b[i] = load_one_raw<ACT>(p.b, row * p.b_st + h);
+    }
+}
+
+// A value of the state after a round trip through the storage format.
+template <int ST>
+__device__ __forceinline__ void round_pair(float& x, float& y)
+{
+    if constexpr (ST != GDN_F32) {
+        const float2 f = unpack_pair<ST>(pack2<ST>(x, y));
+        x = f.x;
+        y = f.y;
+    }
+}
+
+template <int ACT, int ST, int OUT>
+__global__ void __launch_bounds__(NTHREADS)
+__attribute__((amdgpu_waves_per_eu(ST == GDN_F32 ? 1 : 3)))
+gdn_prefill_kernel(const PParams p)
+{
+    constexpr int ESZ = (ST == GDN_F32) ? 4 : 2;
+    constexpr int CH = D * ESZ / 128;
+    constexpr int EPC = 16 / ESZ;
+    constexpr int CSTRIDE = D / CH;
+    static_assert(CH * EPC == NE, "layout");
+    __shared__ __attribute__((aligned(16))) Step sb[2];
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int g = lane >> 3;
+    const int j = lane & 7;
+
+    // XCD-contiguous units: the heads of a sequence share its q/k rows.
+    const int64_t nblk = gridDim.x;
+    const int64_t xcd = blockIdx.x % NXCD;
+    const int64_t per = nblk / NXCD, rem = nblk % NXCD;
+    const int64_t unit = xcd * per + (xcd < rem ? xcd : rem) + blockIdx.x / NXCD;
+    const int64_t seq = unit / p.HV;
+    const int h = static_cast<int>(unit - seq * p.HV);
+    const int kh = h / p.group;
+
+    // ---- metadata; a sequence with any out-of-range field is skipped whole ----
+    const int64_t c0 = p.cu[seq];
+    const int L = static_cast<int>(p.cu[seq + 1] - c0);
+    const int64_t slot = p.state_idx[seq];
+    if (L <= 0 || slot < 0)
+        return;
+    bool bad = slot >= p.num_slots || c0 < 0;
+    for (int t = tid; t < L && !bad; t += NTHREADS) {
+        const int64_t row = p.tix ? static_cast<int64_t>(p.tix[c0 + t]) : c0 + t;
+        bad = row < 0 || row >= p.n_tok;
+    }
+    if (__syncthreads_or(bad))
+        return;
+    const bool init = p.has_init ? p.has_init[seq] != 0 : true;
+
+    // ---- the state: read once (or zero), kept in registers ----
+    const size_t tile = static_cast<size_t>(D) * D;
+    char* sbase = static_cast<char*>(p.pool) +
+                  (static_cast<size_t>(slot) * p.HV + h) * tile * ESZ;
+    float S[RPT][NE];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+        const int row = wave * ROWS_PER_WAVE + r * 8 + g;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            uint4 w = make_uint4(0u, 0u, 0u, 0u);
+            if (init)
+                w = *reinterpret_cast<const uint4*>(
+                    sbase + (static_cast<size_t>(row) * D + c * CSTRIDE + j * EPC) * ESZ);
+            const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                if constexpr (ST == GDN_F32) {
+                    S[r][c * 4 + m] = __uint_as_float(u[m]);
+                } else {
+                    const float2 f = unpack_pair<ST>(u[m]);
+                    S[r][c * 8 + 2 * m] = f.x;
+                    S[r][c * 8 + 2 * m + 1] = f.y;
+                }
+            }
+        }
+    }
+
+    const float A = -expf(p.A_log[h]);
+    const float dtb = p.dt_bias[h];
+    const float2 wn = *reinterpret_cast<const float2*>(p.norm_weight + 2 * lane);
+    const int nsteps = (L + TS - 1) / TS;
+    StepRaw<ACT> raw;
+    issue_step<ACT>(p, c0, L, 0, wave, lane, h, kh, raw);
+
+    for (int step = 0; step < nsteps; ++step) {
+        Step& B = sb[step & 1];
+        const int base = step * TS;
+        const int n = L - base < TS ? L - base : TS;   // tokens in this step
+
+        // ---- prologue: gates, normalised k and q, k^.q^ into LDS ----
+#pragma unroll
+        for (int i = 0; i < NTW; ++i) {
+            const int tl = wave + 4 * i;
+            const float2 qv = unpack_pair<ACT>(raw.q[i]);
+            const float2 kv = unpack_pair<ACT>(raw.k[i]);
+            const float nq = sum64(qv.x * qv.x + qv.y * qv.y);
+            const float nk = sum64(kv.x * kv.x + kv.y * kv.y);
+            const float rk = 1.0f / sqrtf(nk + 1e-6f);
+            const float rq = p.scale / sqrtf(nq + 1e-6f);
+            const float2 kn = make_float2(kv.x * rk, kv.y * rk);
+            const float2 qn = make_float2(qv.x * rq, qv.y * rq);
+            const float kq = sum64(kn.x * qn.x + kn.y * qn.y);
+            if (tl < n) {
+                *reinterpret_cast<float2*>(&B.k[tl][2 * lane]) = kn;
+                *reinterpret_cast<float2*>(&B.q[tl][2 * lane]) = qn;
+                *reinterpret_cast<float2*>(&B.v[tl][2 * lane]) = unpack_pair<ACT>(raw.v[i]);
+                *reinterpret_cast<float2*>(&B.z[tl][2 * lane]) = unpack_pair<ACT>(raw.z[i]);
+                if (lane == 0) {
+                    B.row[tl] = raw.row[i];
+                    const float x = unpack_one<ACT>(raw.a[i]) + dtb;
+                    const float sp = x > 20.0f ? x : log1pf(expf(x));
+                    B.alpha[tl] = expf(A * sp);
+                    B.beta[tl] = 1.0f / (1.0f + expf(-unpack_one<ACT>(raw.b[i])));
+                    B.kq[tl] = kq;
+                }
+            }
+        }
+        // ---- the next step's loads, in flight during this step's tokens ----
+        if (step + 1 < nsteps)
+            issue_step<ACT>(p, c0, L, step + 1, wave, lane, h, kh, raw);
+        __syncthreads();
+
+        // ---- the step's tokens, strictly in order ----
+        for (int tl = 0; tl < n; ++tl) {
+            const float alpha = B.alpha[tl];
+            const float beta = B.beta[tl];
+            const float kq = B.kq[tl];
+            float kn[NE], qn[NE];
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+#pragma unroll
+                for (int m = 0; m < EPC; m += 4) {
+                    const float4 k4 =
+                        *reinterpret_cast<const float4*>(&B.k[tl][c * CSTRIDE + j * EPC + m]);
+                    const float4 q4 =
+                        *reinterpret_cast<const float4*>(&B.q[tl][c * CSTRIDE + j * EPC + m]);
+                    kn[c * EPC + m + 0] = k4.x; kn[c * EPC + m + 1] = k4.y;
+                    kn[c * EPC + m + 2] = k4.z; kn[c * EPC + m + 3] = k4.w;
+                    qn[c * EPC + m + 0] = q4.x; qn[c * EPC + m + 1] = q4.y;
+                    qn[c * EPC + m + 2] = q4.z; qn[c * EPC + m + 3] = q4.w;
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < RPT; ++r) {
+                const int row = wave * ROWS_PER_WAVE + r * 8 + g;
+                float pk = 0.0f, pq = 0.0f;
+#pragma unroll
+                for (int e = 0; e < NE; ++e) {
+                    pk = fmaf(S[r][e], kn[e], pk);
+                    pq = fmaf(S[r][e], qn[e], pq);
+                }
+                pk = sum8(pk);
+                pq = sum8(pq);
+                const float d = beta * (B.v[tl][row] - alpha * pk);
+                const float o = fmaf(alpha, pq, d * kq);
+#pragma unroll
+                for (int e = 0; e < NE; ++e)
+                    S[r][e] = fmaf(d, kn[e], alpha * S[r][e]);
+                if (j == 0)
+                    B.o[tl][row] = o;
+            }
+            // chunk end: the state continues from its stored (rounded) value
+            const int tg = base + tl;
+            if ((tg + 1) % p.chunk == 0 && tg + 1 < L) {
+#pragma unroll
+                for (int r = 0; r < RPT; ++r)
+#pragma unroll
+                    for (int e = 0; e < NE; e += 2)
+                        round_pair<ST>(S[r][e], S[r][e + 1]);
+            }
+        }
+        __syncthreads();
+
+        // ---- gated RMSNorm over V per (token, head) ----
+#pragma unroll
+        for (int i = 0; i < NTW; ++i) {
+            const int tl = wave + 4 * i;
+            if (tl < n) {
+                const float2 o = *reinterpret_cast<const float2*>(&B.o[tl][2 * lane]);
+                const float2 zv = *reinterpret_cast<const float2*>(&B.z[tl][2 * lane]);
+                const int64_t row = B.row[tl];
+                const float ms = sum64(o.x * o.x + o.y * o.y) * (1.0f / D);
+                const float rr = 1.0f / sqrtf(ms + p.norm_eps);
+                const float gx = zv.x / (1.0f + expf(-zv.x));
+                const float gy = zv.y / (1.0f + expf(-zv.y));
+                const float2 y = make_float2(o.x * rr * wn.x * gx, o.y * rr * wn.y * gy);
+                store_pair<OUT>(p.out, row * p.o_st + h * p.o_sh + 2 * lane, y);
+            }
+        }
+    }
+
+    // ---- the final state, rounded once, written once ----
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+        const int row = wave * ROWS_PER_WAVE + r * 8 + g;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            u32x4 w;
+            if constexpr (ST == GDN_F32) {
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                    w[m] = __float_as_uint(S[r][c * 4 + m]);
+            } else {
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                    w[m] = pack2<ST>(S[r][c * 8 + 2 * m], S[r][c * 8 + 2 * m + 1]);
+            }
+            __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(
+                sbase + (static_cast<size_t>(row) * D + c * CSTRIDE + j * EPC) * ESZ));
+        }
+    }
+}
+
+template <int A, int S, int O>
+hipError_t launch_typed(const PParams& p, int64_t grid, hipStream_t stream)
+{
+    PParams args = p;
+    void* argv[] = {&args};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&gdn_prefill_kernel<A, S, O>),
+                           dim3(static_cast<uint32_t>(grid)), dim3(NTHREADS), argv, 0, stream);
+}
+
+template <int A, int S>
+hipError_t launch_out(int out, const PParams& p, int64_t grid, hipStream_t s)
+{
+    switch (out) {
+    case GDN_F32: return launch_typed<A, S, GDN_F32>(p, grid, s);
+    case GDN_F16: return launch_typed<A, S, GDN_F16>(p, grid, s);
+    default: return launch_typed<A, S, GDN_BF16>(p, grid, s);
+    }
+}
+
+template <int A>
+hipError_t launch_state(int st, int out, const PParams& p, int64_t grid, hipStream_t s)
+{
+    switch (st) {
+    case GDN_F32: return launch_out<A, GDN_F32>(out, p, grid, s);
+    case GDN_F16: return launch_out<A, GDN_F16>(out, p, grid, s);
+    default: return launch_out<A, GDN_BF16>(out, p, grid, s);
+    }
+}
+
+hipError_t launch(int act, int st, int out, const PParams& p, int64_t grid, hipStream_t s)
+{
+    switch (act) {
+    case GDN_F32: return launch_state<GDN_F32>(st, out, p, grid, s);
+    case GDN_F16: return launch_state<GDN_F16>(st, out, p, grid, s);
+    default: return launch_state<GDN_BF16>(st, out, p, grid, s);
+    }
+}
+
+}  // namespace
+
+extern "C" gdn_status gdn_prefill_update(const gdn_layer* layer, const gdn_state_pool* pool,
+                                         const int32_t* cu_seqlens, int32_t num_seqs,
+                                         const int32_t* state_indices,
+                                         const int32_t* has_initial_state,
+                                         const int32_t* token_indx, int32_t chunk_size,
+                                         hipStream_t stream)
+{
+    gdn::clear_error();
+    gdn_status st;
+    if ((st = gdn::check_layer(layer)) != GDN_OK || (st = gdn::check_pool(pool)) != GDN_OK)
+        return st;
+    if (num_seqs < 0)
+        return gdn::fail(GDN_ERR_INVALID, "num_seqs is negative");
+    if (chunk_size < 1)
+        return gdn::fail(GDN_ERR_INVALID, "chunk_size must be >= 1");
+    if (num_seqs == 0 || layer->n_tok == 0)
+        return GDN_OK;
+    if (!cu_seqlens || !state_indices)
+        return gdn::fail(GDN_ERR_INVALID, "cu_seqlens or state_indices is NULL");
+    const int64_t grid = static_cast<int64_t>(num_seqs) * layer->num_v_heads;
+    if (grid > 0x7fffffffLL)
+        return gdn::fail(GDN_ERR_INVALID, "num_seqs * num_v_heads exceeds the grid limit");
+    PParams p{};
+    const gdn_layer* L = layer;
+    p.q = L->q.data; p.q_st = L->q.stride_tok; p.q_sh = L->q.stride_head;
+    p.k = L->k.data; p.k_st = L->k.stride_tok; p.k_sh = L->k.stride_head;
+    p.v = L->v.data; p.v_st = L->v.stride_tok; p.v_sh = L->v.stride_head;
+    p.z = L->z.data; p.z_st = L->z.stride_tok; p.z_sh = L->z.stride_head;
+    p.a = L->a.data; p.a_st = L->a.stride_tok;
+    p.b = L->b.data; p.b_st = L->b.stride_tok;
+    p.out = L->out.data; p.o_st = L->out.stride_tok; p.o_sh = L->out.stride_head;
+    p.A_log = L->A_log;
+    p.dt_bias = L->dt_bias;
+    p.norm_weight = L->norm_weight;
+    p.pool = pool->data;
+    p.num_slots = pool->num_slots;
+    p.n_tok = L->n_tok;
+    p.HV = L->num_v_heads;
+    p.group = L->num_v_heads / L->num_k_heads;
+    p.scale = L->scale;
+    p.norm_eps = L->norm_eps;
+    p.cu = cu_seqlens;
+    p.state_idx = state_indices;
+    p.has_init = has_initial_state;
+    p.tix = token_indx;
+    p.chunk = chunk_size;
+    const hipError_t e = launch(L->act_dtype, pool->dtype, L->out_dtype, p, grid, stream);
+    if (e != hipSuccess)
+        return gdn::fail(GDN_ERR_DEVICE, "prefill launch failed: %s", hipGetErrorString(e));
+    return GDN_OK;
+}

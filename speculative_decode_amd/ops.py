@@ -26,7 +26,7 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdn_spec.so")
-ABI_VERSION = 3
+ABI_VERSION = 4
 MAX_DRAFT_TOKENS = 8
 
 GDN_F32, GDN_F16, GDN_BF16 = 0, 1, 2
@@ -96,6 +96,10 @@ SIGNATURES = {
     "gdn_mixed_decode_update": (ctypes.c_int, [ctypes.POINTER(GdnLayer),
                                                ctypes.POINTER(GdnStatePool), _VP, _I32, _I32,
                                                _VP, _I32, _VP, _VP, _VP, _I32, _VP, _VP]),
+    "gdn_prefill_update": (ctypes.c_int, [ctypes.POINTER(GdnLayer),
+                                          ctypes.POINTER(GdnStatePool), _VP, _I32, _VP, _VP,
+                                          _VP, _I32, _VP]),
+    "gdn_validate_prefill_indices_host": (ctypes.c_int, [_I64, _I64, _VP, _I32, _VP, _VP]),
     "gdn_validate_indices_host": (ctypes.c_int, [_I64, _I64, _VP, _I32, _I32, _VP, _I32,
                                                  _VP, _VP, _VP, _I32, _VP]),
     "gdn_last_error": (ctypes.c_char_p, []),
@@ -342,6 +346,59 @@ def forward_core(q, k, v, z, a, b, A_log, dt_bias, norm_weight, state, *,
                       non_spec_state_indices, token_indx=non_spec_token_indx, out=out,
                       scale=scale, norm_eps=norm_eps)
     return out
+
+
+def prefill_update(q, k, v, z, a, b, A_log, dt_bias, norm_weight, state, cu_seqlens,
+                   state_indices, *, has_initial_state=None, token_indx=None, out=None,
+                   chunk_size=64, scale=None, norm_eps=1e-5):
+    """Chunked prefill of ``state`` in place (one slot per sequence, the state
+    rounded to its dtype every ``chunk_size`` rows); returns ``out`` (default
+    zeros)."""
+    lib = load_library()
+    if out is None:
+        out = torch.zeros_like(z)
+    dev = q.device
+    layer = make_layer(q, k, v, z, a, b, A_log, dt_bias, norm_weight, out,
+                       scale=scale, norm_eps=norm_eps)
+    pool = make_pool(state)
+    cu = _meta(cu_seqlens, "cu_seqlens", dev)
+    si = _meta(state_indices, "state_indices", dev)
+    hi = _meta(has_initial_state, "has_initial_state", dev)
+    ti = _meta(token_indx, "token_indx", dev)
+    B = cu.shape[0] - 1
+    if si.shape[0] != B or (hi is not None and hi.shape[0] != B):
+        raise ValueError("cu_seqlens, state_indices, has_initial_state disagree on B")
+    _check(lib.gdn_prefill_update(ctypes.byref(layer), ctypes.byref(pool), _ptr(cu), B, _ptr(si),
+                                  _ptr(hi), _ptr(ti), int(chunk_size), _stream(dev)))
+    return out
+
+
+def validate_prefill_indices(num_slots: int, n_tok: int, cu_seqlens, state_indices, *,
+                             token_indx=None):
+    """Check prefill metadata on host copies (gdn_validate_prefill_indices_host)."""
+    lib = load_library()
+
+    def host(t):
+        return None if t is None else t.detach().to("cpu", torch.int32).contiguous()
+
+    cu, si, ti = host(cu_seqlens), host(state_indices), host(token_indx)
+    _check(lib.gdn_validate_prefill_indices_host(int(num_slots), int(n_tok), _ptr(cu),
+                                                 cu.shape[0] - 1, _ptr(si), _ptr(ti)))
+
+
+def prefill_batch_args(batch, device, *, state=None, out=None):
+    """Device copies of a workloads.PrefillBatch as keyword arguments of
+    prefill_update."""
+    def d(t):
+        return None if t is None else t.to(device)
+    return dict(q=d(batch.q), k=d(batch.k), v=d(batch.v), z=d(batch.z), a=d(batch.a),
+                b=d(batch.b), A_log=d(batch.A_log), dt_bias=d(batch.dt_bias),
+                norm_weight=d(batch.norm_weight),
+                state=d(batch.pool) if state is None else state,
+                cu_seqlens=d(batch.cu_seqlens), state_indices=d(batch.state_indices),
+                has_initial_state=d(batch.has_initial_state), token_indx=d(batch.token_indx),
+                out=out, chunk_size=batch.chunk_size, scale=batch.scale,
+                norm_eps=batch.norm_eps)
 
 
 def validate_indices(num_slots: int, n_tok: int, *, cu_seqlens=None, spec_state_indices=None,

@@ -264,3 +264,31 @@ def test_mixed_entry_errors_and_no_op(lib):
     assert f(*args(0, 2, ns=None)) == 1 and "state_indices" in ops.last_error()
     assert f(*args(1, 1, mql=9)) == 2 and "exceeds" in ops.last_error()
     assert f(*args(1, 1, mql=0)) == 1
+
+
+def test_prefill_entry_errors_and_validator(lib):
+    layer, pool, keep = _layer_and_pool()
+    m = torch.zeros(16, dtype=torch.int32)
+    p = ctypes.c_void_p(m.data_ptr())
+    f = lib.gdn_prefill_update
+    assert f(ctypes.byref(layer), ctypes.byref(pool), None, 0, None, None, None, 64, None) == 0
+    assert f(ctypes.byref(layer), ctypes.byref(pool), p, -1, p, None, None, 64, None) == 1
+    assert f(ctypes.byref(layer), ctypes.byref(pool), p, 1, p, None, None, 0, None) == 1
+    assert "chunk_size" in ops.last_error()
+    assert f(ctypes.byref(layer), ctypes.byref(pool), None, 1, p, None, None, 64, None) == 1
+    b = workloads.make_prefill("prefill_small")
+    ops.validate_prefill_indices(b.pool.shape[0], b.n_tok, b.cu_seqlens, b.state_indices)
+    si = b.state_indices.clone()
+    si[3] = si[0]
+    with pytest.raises(ops.GdnError) as ei:
+        ops.validate_prefill_indices(b.pool.shape[0], b.n_tok, b.cu_seqlens, si)
+    assert "two sequences" in ei.value.reason
+    si[3] = b.pool.shape[0]
+    with pytest.raises(ops.GdnError):
+        ops.validate_prefill_indices(b.pool.shape[0], b.n_tok, b.cu_seqlens, si)
+    tix = torch.arange(b.n_tok, dtype=torch.int32)
+    tix[5] = tix[6]
+    with pytest.raises(ops.GdnError) as ei:
+        ops.validate_prefill_indices(b.pool.shape[0], b.n_tok, b.cu_seqlens, b.state_indices,
+                                     token_indx=tix)
+    assert "used twice" in ei.value.reason
