@@ -9,9 +9,11 @@
 // chunk's state is written back.  gdn_spec.h spells out the formula.
 //
 // How it is computed here:
-//   * One 256-thread workgroup per (sequence, value head), the 128 x 128
-//     state in registers exactly as in the decode kernel (each 8-lane group
-//     owns a row at a time, each lane 16 elements of 4 rows).  The state is
+//   * One 512-thread workgroup per (sequence, value head), the 128 x 128
+//     state in registers with the decode kernel's lane layout (each 8-lane
+//     group owns a row at a time, each lane 16 elements), spread over eight
+//     waves -- 2 rows per lane -- so that a SIMD has more waves to hide the
+//     latency of each token's LDS reads and reductions.  The state is
 //     read once, rounded in registers at every chunk end, and written once:
 //     intermediate chunk write-backs go to the same slot and are overwritten,
 //     so only the rounding is kept, not the stores.
@@ -39,13 +41,15 @@ namespace {
 using namespace gdn_dev;
 
 constexpr int D = GDN_HEAD_DIM;
-constexpr int NTHREADS = 256;
-constexpr int ROWS_PER_WAVE = D / (NTHREADS / 64);   // 32
-constexpr int RPT = ROWS_PER_WAVE / 8;               // rows per thread: 4
+constexpr int NTHREADS = 512;
+constexpr int NWAVES = NTHREADS / 64;
+constexpr int ROWS_PER_WAVE = D / NWAVES;
+constexpr int RPT = ROWS_PER_WAVE / 8;               // rows per thread
 constexpr int NE = D / 8;                            // elements per (thread, row): 16
 constexpr int NXCD = 8;
 constexpr int TS = 8;                                // tokens per step
-constexpr int NTW = TS / 4;                          // tokens per wave per step
+constexpr int NTW = TS / NWAVES;                     // tokens per wave per step
+static_assert(TS % NWAVES == 0 && RPT >= 1, "geometry");
 
 struct PParams {
     const void* q;
@@ -85,7 +89,7 @@ struct Step {
     int64_t row[TS];
 };
 
-// The raw activations of one step for one wave (tokens wave, wave + 4).
+// The raw activations of one step for one wave (tokens wave, wave + NWAVES, ...).
 template <int ACT>
 struct StepRaw {
     typename Pair<ACT>::raw q[NTW], k[NTW], v[NTW], z[NTW];
@@ -99,7 +103,7 @@ __device__ __forceinline__ void issue_step(const PParams& p, int64_t c0, int L, 
 {
 #pragma unroll
     for (int i = 0; i < NTW; ++i) {
-        const int t = step * TS + wave + 4 * i;
+        const int t = step * TS + wave + NWAVES * i;
         const int tt = t < L ? t : L - 1;        // clamped: always a valid row
         const int64_t row = p.tix ? static_cast<int64_t>(p.tix[c0 + tt]) : c0 + tt;
         r.row[i] = row;
@@ -125,7 +129,7 @@ __device__ __forceinline__ void round_pair(float& x, float& y)
 
 template <int ACT, int ST, int OUT>
 __global__ void __launch_bounds__(NTHREADS)
-__attribute__((amdgpu_waves_per_eu(ST == GDN_F32 ? 1 : 3)))
+__attribute__((amdgpu_waves_per_eu(ST == GDN_F32 ? 2 : 4)))
 gdn_prefill_kernel(const PParams p)
 {
     constexpr int ESZ = (ST == GDN_F32) ? 4 : 2;
@@ -208,7 +212,7 @@ gdn_prefill_kernel(const PParams p)
         // ---- prologue: gates, normalised k and q, k^.q^ into LDS ----
 #pragma unroll
         for (int i = 0; i < NTW; ++i) {
-            const int tl = wave + 4 * i;
+            const int tl = wave + NWAVES * i;
             const float2 qv = unpack_pair<ACT>(raw.q[i]);
             const float2 kv = unpack_pair<ACT>(raw.k[i]);
             const float nq = sum64(qv.x * qv.x + qv.y * qv.y);
@@ -292,7 +296,7 @@ gdn_prefill_kernel(const PParams p)
         // ---- gated RMSNorm over V per (token, head) ----
 #pragma unroll
         for (int i = 0; i < NTW; ++i) {
-            const int tl = wave + 4 * i;
+            const int tl = wave + NWAVES * i;
             if (tl < n) {
                 const float2 o = *reinterpret_cast<const float2*>(&B.o[tl][2 * lane]);
                 const float2 zv = *reinterpret_cast<const float2*>(&B.z[tl][2 * lane]);
