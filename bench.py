@@ -265,7 +265,8 @@ def main():
     traffic = recorded_traffic(args.workload, "gdn")
     ms_per_step = gpu_ms / args.steps
     cpu = cpu_baseline(batch, min(args.cpu_seqs, batch.num_seqs)) if args.cpu_seqs > 0 else None
-    dtypes = {torch.float32: "f32", torch.bfloat16: "bf16", torch.float16: "f16"}
+    dtypes = {torch.float32: "f32", torch.bfloat16: "bf16", torch.float16: "f16",
+              torch.float8_e4m3fn: "f8e4m3"}
     line = {
         "metric": "draft tokens/sec and achieved HBM GB/s (% of peak), B=128 T=8 BF16 state",
         "value": tokens * args.steps / (gpu_ms * 1e-3),
@@ -324,7 +325,8 @@ def bench_conv(args, dev):
     tokens = batch.draft_tokens()
     alg_bytes = batch.algorithmic_bytes()
     achieved = alg_bytes / (avg_ms * 1e-3) / 1e9
-    dtypes = {torch.float32: "f32", torch.bfloat16: "bf16", torch.float16: "f16"}
+    dtypes = {torch.float32: "f32", torch.bfloat16: "bf16", torch.float16: "f16",
+              torch.float8_e4m3fn: "f8e4m3"}
     line = {
         "metric": "conv update with rewind: draft tokens/sec and achieved HBM GB/s "
                   "(% of peak), B=128 T=8",

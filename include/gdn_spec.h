@@ -74,11 +74,15 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 4
+#define GDN_ABI_VERSION 5
 #define GDN_MAX_DRAFT_TOKENS 8
 #define GDN_HEAD_DIM 128
 
-typedef enum { GDN_F32 = 0, GDN_F16 = 1, GDN_BF16 = 2 } gdn_dtype;
+/* GDN_F8E4M3 (OCP FP8 E4M3 without infinities, largest finite 448) is a
+ * state-pool format only: #52191 风险与影响 notes that the state type leaves
+ * room for FP8, halving the state bytes again.  Stores round to nearest even
+ * and saturate to +-448 (NaN stays NaN); loads are exact. */
+typedef enum { GDN_F32 = 0, GDN_F16 = 1, GDN_BF16 = 2, GDN_F8E4M3 = 3 } gdn_dtype;
 
 typedef enum {
     GDN_OK = 0,
@@ -123,7 +127,8 @@ typedef struct {
 } gdn_layer;
 
 /* The recurrent-state pool, contiguous [num_slots][num_v_heads][V][K]
- * (K innermost), updated in place.  16-byte aligned. */
+ * (K innermost), updated in place.  16-byte aligned.  dtype: fp32, fp16, bf16
+ * or fp8 e4m3. */
 typedef struct {
     void*   data;
     int32_t dtype;        /* gdn_dtype */
@@ -238,6 +243,15 @@ gdn_status gdn_validate_indices_host(int64_t num_slots, int64_t n_tok,
                                      const int32_t* state_indices,
                                      int32_t num_non_spec,
                                      const int32_t* non_spec_token_indx);
+
+/*
+ * Rounds n fp32 values (device pointer src) into the state format `dtype`
+ * at dst (device pointer, n elements), with the conversion every kernel of
+ * this library uses at a state store: nearest even, FP8 saturating to +-448.
+ * For filling a pool from FP32 states; one kernel on `stream`.
+ */
+gdn_status gdn_cast_to_state(const float* src, void* dst, int64_t n, int32_t dtype,
+                             hipStream_t stream);
 
 /* Reason for the last non-OK status returned on this thread ("" if none). */
 const char* gdn_last_error(void);

@@ -26,9 +26,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRCS = [os.path.join(_HERE, "gdn_oracle.c"), os.path.join(_HERE, "conv_oracle.c")]
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
-FMT_F32, FMT_F16, FMT_BF16, FMT_F64 = 0, 1, 2, 3
+FMT_F32, FMT_F16, FMT_BF16, FMT_F64, FMT_F8E4M3 = 0, 1, 2, 3, 4
 _FMT = {torch.float32: FMT_F32, torch.float16: FMT_F16,
-        torch.bfloat16: FMT_BF16, torch.float64: FMT_F64}
+        torch.bfloat16: FMT_BF16, torch.float64: FMT_F64,
+        torch.float8_e4m3fn: FMT_F8E4M3}
 _ERR = {1: "bad argument", 2: "index out of range", 3: "out of memory"}
 
 _lib = None

@@ -65,7 +65,7 @@ double orc_round(int fmt, double x);   /* gdn_oracle.c */
 enum { CONV_OK = 0, CONV_BAD_ARG = 1, CONV_BAD_INDEX = 2, CONV_NO_MEMORY = 3 };
 enum { CONV_ACT_NONE = 0, CONV_ACT_SILU = 1 };
 
-static int fmt_valid(int f) { return f >= 0 && f <= 3; }
+static int fmt_valid(int f) { return f >= 0 && f <= 4; }
 
 static double activate(int act, double s)
 {

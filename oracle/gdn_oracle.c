@@ -52,7 +52,8 @@
 #include <string.h>
 
 /* Storage formats understood by orc_round. */
-enum { ORC_FMT_F32 = 0, ORC_FMT_F16 = 1, ORC_FMT_BF16 = 2, ORC_FMT_F64 = 3 };
+enum { ORC_FMT_F32 = 0, ORC_FMT_F16 = 1, ORC_FMT_BF16 = 2, ORC_FMT_F64 = 3,
+       ORC_FMT_F8E4M3 = 4 };
 
 /* Return codes. */
 enum { ORC_OK = 0, ORC_BAD_ARG = 1, ORC_BAD_INDEX = 2, ORC_NO_MEMORY = 3 };
@@ -68,6 +69,11 @@ enum { ORC_OK = 0, ORC_BAD_ARG = 1, ORC_BAD_INDEX = 2, ORC_NO_MEMORY = 3 };
  *   f32     24                2^-126           2^-149             (2-2^-23)*2^127
  *   f16     11                2^-14            2^-24              65504
  *   bf16     8                2^-126           2^-133             (2-2^-7)*2^127
+ *   fp8 e4m3 4                2^-6             2^-9               448
+ * The FP8 state format is OCP E4M3 without infinities; the reports only say
+ * the state type leaves room for FP8, so the plainest reading is taken:
+ * nearest-even, and values beyond 448 (infinities included) saturate to
+ * +-448 rather than becoming NaN, which a recurrent state would never shed.
  */
 double orc_round(int fmt, double x)
 {
@@ -81,8 +87,11 @@ double orc_round(int fmt, double x)
     case ORC_FMT_F32: p = 24; emin = -126; maxfin = ldexp(2.0 - ldexp(1.0, -23), 127); break;
     case ORC_FMT_F16: p = 11; emin = -14;  maxfin = 65504.0; break;
     case ORC_FMT_BF16: p = 8; emin = -126; maxfin = ldexp(2.0 - ldexp(1.0, -7), 127); break;
+    case ORC_FMT_F8E4M3: p = 4; emin = -6; maxfin = 448.0; break;
     default: return NAN;
     }
+    if (fmt == ORC_FMT_F8E4M3 && isinf(x))
+        return x > 0 ? maxfin : -maxfin;
     if (isnan(x) || isinf(x) || x == 0.0)
         return x;
     /* x = m * 2^e with 0.5 <= |m| < 1, so |x| lies in [2^(e-1), 2^e). */
@@ -94,8 +103,11 @@ double orc_round(int fmt, double x)
     /* Scaling by a power of two is exact; nearbyint rounds ties to even in
      * the default rounding mode. */
     r = ldexp(nearbyint(ldexp(x, -q)), q);
-    if (fabs(r) > maxfin)
+    if (fabs(r) > maxfin) {
+        if (fmt == ORC_FMT_F8E4M3)
+            return x > 0 ? maxfin : -maxfin;
         return x > 0 ? INFINITY : -INFINITY;
+    }
     return r;
 }
 
@@ -271,7 +283,7 @@ static int layer_ok(const layer_t *L)
 static int fmt_ok(int f)
 {
     return f == ORC_FMT_F32 || f == ORC_FMT_F16 || f == ORC_FMT_BF16 ||
-           f == ORC_FMT_F64;
+           f == ORC_FMT_F64 || f == ORC_FMT_F8E4M3;
 }
 
 /*

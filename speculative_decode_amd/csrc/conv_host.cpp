@@ -17,7 +17,8 @@ gdn_status check_conv_layer(const gdn_conv_layer* L)
 {
     if (!L)
         return fail(GDN_ERR_INVALID, "conv layer is NULL");
-    const int ex = dtype_size(L->x_dtype), eo = dtype_size(L->out_dtype);
+    const int ex = L->x_dtype == GDN_F8E4M3 ? 0 : dtype_size(L->x_dtype);
+    const int eo = L->out_dtype == GDN_F8E4M3 ? 0 : dtype_size(L->out_dtype);
     if (!ex)
         return fail(GDN_ERR_UNSUPPORTED, "x_dtype %d is not f32/f16/bf16", L->x_dtype);
     if (!eo)

@@ -32,6 +32,7 @@ int dtype_size(int32_t dt)
     case GDN_F32: return 4;
     case GDN_F16: return 2;
     case GDN_BF16: return 2;
+    case GDN_F8E4M3: return 1;
     default: return 0;
     }
 }
@@ -62,7 +63,8 @@ gdn_status check_layer(const gdn_layer* L)
 {
     if (!L)
         return fail(GDN_ERR_INVALID, "layer is NULL");
-    const int ea = dtype_size(L->act_dtype), eo = dtype_size(L->out_dtype);
+    const int ea = L->act_dtype == GDN_F8E4M3 ? 0 : dtype_size(L->act_dtype);
+    const int eo = L->out_dtype == GDN_F8E4M3 ? 0 : dtype_size(L->out_dtype);
     if (!ea)
         return fail(GDN_ERR_UNSUPPORTED, "act_dtype %d is not f32/f16/bf16", L->act_dtype);
     if (!eo)
@@ -112,7 +114,7 @@ gdn_status check_pool(const gdn_state_pool* P)
     if (!P)
         return fail(GDN_ERR_INVALID, "pool is NULL");
     if (!dtype_size(P->dtype))
-        return fail(GDN_ERR_UNSUPPORTED, "state dtype %d is not f32/f16/bf16", P->dtype);
+        return fail(GDN_ERR_UNSUPPORTED, "state dtype %d is not f32/f16/bf16/f8e4m3", P->dtype);
     if (!P->data)
         return fail(GDN_ERR_INVALID, "pool.data is NULL");
     if (!aligned(P->data, 16))

@@ -92,10 +92,10 @@ template <int ACT, int ST, int OUT, bool SPEC>
 __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(ST == GDN_F32 ? 1 : 4)))
 gdn_update_kernel(const KParams p)
 {
-    constexpr int ESZ = (ST == GDN_F32) ? 4 : 2;   // state element bytes
-    constexpr int CH = D * ESZ / 128;              // 16-byte chunks per (thread,row): 4 or 2
-    constexpr int EPC = 16 / ESZ;                  // elements per chunk: 4 or 8
-    constexpr int CSTRIDE = D / CH;                // row offset between chunks: 32 or 64
+    constexpr int ESZ = ST == GDN_F32 ? 4 : (ST == GDN_F8E4M3 ? 1 : 2);   // state bytes
+    constexpr int CH = D * ESZ / 128;              // 16-byte chunks per (thread,row): 4, 2, 1
+    constexpr int EPC = 16 / ESZ;                  // elements per chunk: 4, 8, 16
+    constexpr int CSTRIDE = D / CH;                // row offset between chunks: 32, 64, 128
     constexpr int NT = SPEC ? MAXT : 1;            // static bound on draft tokens
     static_assert(CH * EPC == NE, "layout");
 
@@ -253,22 +253,10 @@ gdn_update_kernel(const KParams p)
     // ---- tile to fp32 registers ----
     float S[RPT][NE];
 #pragma unroll
-    for (int r = 0; r < RPT; ++r) {
+    for (int r = 0; r < RPT; ++r)
 #pragma unroll
-        for (int c = 0; c < CH; ++c) {
-            const uint32_t w[4] = {raw[r][c].x, raw[r][c].y, raw[r][c].z, raw[r][c].w};
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                if constexpr (ST == GDN_F32) {
-                    S[r][c * 4 + m] = __uint_as_float(w[m]);
-                } else {
-                    const float2 f = unpack_pair<ST>(w[m]);
-                    S[r][c * 8 + 2 * m] = f.x;
-                    S[r][c * 8 + 2 * m + 1] = f.y;
-                }
-            }
-        }
-    }
+        for (int c = 0; c < CH; ++c)
+            chunk_to_f32<ST>(raw[r][c], &S[r][c * EPC]);
 
     // ---- the draft tokens, strictly in order (unrolled: the tile stays in
     // the same registers from token to token) ----
@@ -315,25 +303,27 @@ gdn_update_kernel(const KParams p)
                 S[r][e] = fmaf(d, kn[e], alpha * S[r][e]);
             if (j == 0)
                 sO[t][row] = o;
+            if constexpr (ST != GDN_F8E4M3) {
 #pragma unroll
-            for (int c = 0; c < CH; ++c) {
-                uint4 w;
-                if constexpr (ST == GDN_F32) {
-                    w.x = __float_as_uint(S[r][c * 4 + 0]);
-                    w.y = __float_as_uint(S[r][c * 4 + 1]);
-                    w.z = __float_as_uint(S[r][c * 4 + 2]);
-                    w.w = __float_as_uint(S[r][c * 4 + 3]);
-                } else {
-                    w.x = pack2<ST>(S[r][c * 8 + 0], S[r][c * 8 + 1]);
-                    w.y = pack2<ST>(S[r][c * 8 + 2], S[r][c * 8 + 3]);
-                    w.z = pack2<ST>(S[r][c * 8 + 4], S[r][c * 8 + 5]);
-                    w.w = pack2<ST>(S[r][c * 8 + 6], S[r][c * 8 + 7]);
+                for (int c = 0; c < CH; ++c) {
+                    // Streaming store: the tile is not read again in this
+                    // launch, so it should not displace anything in L2 / MALL.
+                    __builtin_nontemporal_store(f32_to_chunk<ST>(&S[r][c * EPC]),
+                        reinterpret_cast<u32x4*>(
+                            wbase + (static_cast<size_t>(row) * D + c * CSTRIDE + j * EPC) * ESZ));
                 }
-                // Streaming store: the tile is not read again in this launch,
-                // so it should not displace anything in L2 / MALL.
-                const u32x4 wv = {w.x, w.y, w.z, w.w};
-                __builtin_nontemporal_store(wv, reinterpret_cast<u32x4*>(
-                    wbase + (static_cast<size_t>(row) * D + c * CSTRIDE + j * EPC) * ESZ));
+            }
+        }
+        if constexpr (ST == GDN_F8E4M3) {
+            // One 16-byte chunk per row; encoded together so that the check
+            // for saturation is taken once per token.
+            u32x4 w8[RPT] = {};
+            encode_f8_rows<RPT>(S, w8);
+#pragma unroll
+            for (int r = 0; r < RPT; ++r) {
+                const int row = wave * ROWS_PER_WAVE + r * 8 + g;
+                __builtin_nontemporal_store(w8[r], reinterpret_cast<u32x4*>(
+                    wbase + (static_cast<size_t>(row) * D + j * EPC) * ESZ));
             }
         }
     }
@@ -414,9 +404,12 @@ constexpr int ROUND_BLOCKS_PER_CU = 4;
 // rate drops: seven- and eight-token units run best one per CU, two- to
 // six-token units two per CU.  Single-token units read as much as they write
 // and need the concurrency to hide their read latency, so they run uncapped.
-int blocks_per_cu_for(int writes)
+// An FP8 pool moves half the bytes of a 16-bit one for the same arithmetic,
+// which then sets the pace: its launches run uncapped, so that more waves
+// per SIMD hide each other's instruction latency.
+int blocks_per_cu_for(int writes, int state_dtype)
 {
-    if (writes <= 1)
+    if (writes <= 1 || state_dtype == GDN_F8E4M3)
         return 0;
     return writes <= 6 ? 2 : 1;
 }
@@ -428,10 +421,10 @@ int blocks_per_cu_for(int writes)
 // stores of a finishing block still drain while the CU's next block loads.
 // A smaller batch keeps every unit resident at once.
 template <int NT>
-hipError_t plan_lds(int64_t nunits, int writes, size_t* lds)
+hipError_t plan_lds(int64_t nunits, int writes, int state_dtype, size_t* lds)
 {
     *lds = 0;
-    const int n = blocks_per_cu_for(writes);
+    const int n = blocks_per_cu_for(writes, state_dtype);
     if (n == 0)
         return hipSuccess;
     DeviceInfo d;
@@ -450,7 +443,7 @@ template <int A, int S, int O, bool SPEC>
 hipError_t launch_typed(const KParams& p, int64_t grid, hipStream_t stream)
 {
     size_t lds = 0;
-    hipError_t e = plan_lds<SPEC ? MAXT : 1>(grid, p.max_writes, &lds);
+    hipError_t e = plan_lds<SPEC ? MAXT : 1>(grid, p.max_writes, S, &lds);
     if (e != hipSuccess)
         return e;
     KParams args = p;
@@ -475,6 +468,7 @@ hipError_t launch_state(int st, int out, const KParams& p, int64_t grid, hipStre
     switch (st) {
     case GDN_F32: return launch_out<A, GDN_F32, SPEC>(out, p, grid, s);
     case GDN_F16: return launch_out<A, GDN_F16, SPEC>(out, p, grid, s);
+    case GDN_F8E4M3: return launch_out<A, GDN_F8E4M3, SPEC>(out, p, grid, s);
     default: return launch_out<A, GDN_BF16, SPEC>(out, p, grid, s);
     }
 }
@@ -510,6 +504,37 @@ KParams make_params(const gdn_layer* L, const gdn_state_pool* P)
     p.scale = L->scale;
     p.norm_eps = L->norm_eps;
     return p;
+}
+
+// fp32 -> state format with the store conversion of the kernels above (for
+// FP8, the same 16-element encoder as the token loop, one group per thread).
+template <int DT>
+__global__ void __launch_bounds__(256) cast_kernel(const float* src, void* dst, int64_t n)
+{
+    constexpr int G = DT == GDN_F8E4M3 ? 16 : 1;   // elements per thread and step
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * 256 * G;
+    for (int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * G; i < n;
+         i += stride) {
+        if constexpr (DT == GDN_F8E4M3) {
+            float f[1][16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                f[0][e] = i + e < n ? src[i + e] : 0.0f;
+            u32x4 w[1] = {};
+            encode_f8_rows<1>(f, w);
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                if (i + e < n)
+                    static_cast<uint8_t*>(dst)[i + e] =
+                        static_cast<uint8_t>(w[0][e >> 2] >> (8 * (e & 3)));
+        } else {
+            const float x = src[i];
+            if constexpr (DT == GDN_F32)
+                static_cast<float*>(dst)[i] = x;
+            else
+                static_cast<uint16_t*>(dst)[i] = static_cast<uint16_t>(pack2<DT>(x, 0.f) & 0xffffu);
+        }
+    }
 }
 
 gdn_status device_status(hipError_t e)
@@ -637,4 +662,30 @@ extern "C" gdn_status gdn_decode_update(const gdn_layer* layer, const gdn_state_
     p.max_writes = 1;
     return device_status(
         launch<false>(layer->act_dtype, pool->dtype, layer->out_dtype, p, grid, stream));
+}
+
+extern "C" gdn_status gdn_cast_to_state(const float* src, void* dst, int64_t n, int32_t dtype,
+                                        hipStream_t stream)
+{
+    gdn::clear_error();
+    if (n < 0)
+        return gdn::fail(GDN_ERR_INVALID, "n is negative");
+    if (!gdn::dtype_size(dtype))
+        return gdn::fail(GDN_ERR_UNSUPPORTED, "dtype %d is not f32/f16/bf16/f8e4m3", dtype);
+    if (n == 0)
+        return GDN_OK;
+    if (!src || !dst)
+        return gdn::fail(GDN_ERR_INVALID, "src or dst is NULL");
+    const int64_t per_thread = dtype == GDN_F8E4M3 ? 16 : 1;
+    const int64_t blocks = (n + 256 * per_thread - 1) / (256 * per_thread);
+    const uint32_t grid = static_cast<uint32_t>(blocks < 65536 ? blocks : 65536);
+    void* argv[] = {&src, &dst, &n};
+    const void* fn;
+    switch (dtype) {
+    case GDN_F32: fn = reinterpret_cast<const void*>(&cast_kernel<GDN_F32>); break;
+    case GDN_F16: fn = reinterpret_cast<const void*>(&cast_kernel<GDN_F16>); break;
+    case GDN_BF16: fn = reinterpret_cast<const void*>(&cast_kernel<GDN_BF16>); break;
+    default: fn = reinterpret_cast<const void*>(&cast_kernel<GDN_F8E4M3>); break;
+    }
+    return device_status(hipLaunchKernel(fn, dim3(grid), dim3(256), argv, 0, stream));
 }

@@ -116,23 +116,12 @@ __device__ __forceinline__ void issue_step(const PParams& p, int64_t c0, int L, 
     }
 }
 
-// A value of the state after a round trip through the storage format.
-template <int ST>
-__device__ __forceinline__ void round_pair(float& x, float& y)
-{
-    if constexpr (ST != GDN_F32) {
-        const float2 f = unpack_pair<ST>(pack2<ST>(x, y));
-        x = f.x;
-        y = f.y;
-    }
-}
-
 template <int ACT, int ST, int OUT>
 __global__ void __launch_bounds__(NTHREADS)
 __attribute__((amdgpu_waves_per_eu(ST == GDN_F32 ? 2 : 4)))
 gdn_prefill_kernel(const PParams p)
 {
-    constexpr int ESZ = (ST == GDN_F32) ? 4 : 2;
+    constexpr int ESZ = ST == GDN_F32 ? 4 : (ST == GDN_F8E4M3 ? 1 : 2);
     constexpr int CH = D * ESZ / 128;
     constexpr int EPC = 16 / ESZ;
     constexpr int CSTRIDE = D / CH;
@@ -183,17 +172,7 @@ gdn_prefill_kernel(const PParams p)
             if (init)
                 w = *reinterpret_cast<const uint4*>(
                     sbase + (static_cast<size_t>(row) * D + c * CSTRIDE + j * EPC) * ESZ);
-            const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                if constexpr (ST == GDN_F32) {
-                    S[r][c * 4 + m] = __uint_as_float(u[m]);
-                } else {
-                    const float2 f = unpack_pair<ST>(u[m]);
-                    S[r][c * 8 + 2 * m] = f.x;
-                    S[r][c * 8 + 2 * m + 1] = f.y;
-                }
-            }
+            chunk_to_f32<ST>(w, &S[r][c * EPC]);
         }
     }
 
@@ -316,20 +295,10 @@ gdn_prefill_kernel(const PParams p)
     for (int r = 0; r < RPT; ++r) {
         const int row = wave * ROWS_PER_WAVE + r * 8 + g;
 #pragma unroll
-        for (int c = 0; c < CH; ++c) {
-            u32x4 w;
-            if constexpr (ST == GDN_F32) {
-#pragma unroll
-                for (int m = 0; m < 4; ++m)
-                    w[m] = __float_as_uint(S[r][c * 4 + m]);
-            } else {
-#pragma unroll
-                for (int m = 0; m < 4; ++m)
-                    w[m] = pack2<ST>(S[r][c * 8 + 2 * m], S[r][c * 8 + 2 * m + 1]);
-            }
-            __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(
-                sbase + (static_cast<size_t>(row) * D + c * CSTRIDE + j * EPC) * ESZ));
-        }
+        for (int c = 0; c < CH; ++c)
+            __builtin_nontemporal_store(f32_to_chunk<ST>(&S[r][c * EPC]),
+                reinterpret_cast<u32x4*>(
+                    sbase + (static_cast<size_t>(row) * D + c * CSTRIDE + j * EPC) * ESZ));
     }
 }
 
@@ -358,6 +327,7 @@ hipError_t launch_state(int st, int out, const PParams& p, int64_t grid, hipStre
     switch (st) {
     case GDN_F32: return launch_out<A, GDN_F32>(out, p, grid, s);
     case GDN_F16: return launch_out<A, GDN_F16>(out, p, grid, s);
+    case GDN_F8E4M3: return launch_out<A, GDN_F8E4M3>(out, p, grid, s);
     default: return launch_out<A, GDN_BF16>(out, p, grid, s);
     }
 }

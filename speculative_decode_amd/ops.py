@@ -26,11 +26,13 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdn_spec.so")
-ABI_VERSION = 4
+ABI_VERSION = 5
 MAX_DRAFT_TOKENS = 8
 
-GDN_F32, GDN_F16, GDN_BF16 = 0, 1, 2
+GDN_F32, GDN_F16, GDN_BF16, GDN_F8E4M3 = 0, 1, 2, 3
 _DTYPE = {torch.float32: GDN_F32, torch.float16: GDN_F16, torch.bfloat16: GDN_BF16}
+_STATE_DTYPE = dict(_DTYPE)
+_STATE_DTYPE[torch.float8_e4m3fn] = GDN_F8E4M3
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_INVALID", 2: "GDN_ERR_UNSUPPORTED", 3: "GDN_ERR_DEVICE"}
 
 
@@ -102,6 +104,7 @@ SIGNATURES = {
     "gdn_validate_prefill_indices_host": (ctypes.c_int, [_I64, _I64, _VP, _I32, _VP, _VP]),
     "gdn_validate_indices_host": (ctypes.c_int, [_I64, _I64, _VP, _I32, _I32, _VP, _I32,
                                                  _VP, _VP, _VP, _I32, _VP]),
+    "gdn_cast_to_state": (ctypes.c_int, [_VP, _VP, _I64, _I32, _VP]),
     "gdn_last_error": (ctypes.c_char_p, []),
     "gdn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "gdn_abi_version": (ctypes.c_int32, []),
@@ -220,11 +223,25 @@ def make_layer(q, k, v, z, a, b, A_log, dt_bias, norm_weight, out, *, scale=None
 
 
 def make_pool(state: torch.Tensor) -> GdnStatePool:
-    if state.dtype not in _DTYPE:
-        raise ValueError("state pool must be float32, float16 or bfloat16")
+    if state.dtype not in _STATE_DTYPE:
+        raise ValueError("state pool must be float32, float16, bfloat16 or float8_e4m3fn")
     if state.dim() != 4 or not state.is_contiguous():
         raise ValueError("state pool must be a contiguous [num_slots, HV, V, K] tensor")
-    return GdnStatePool(state.data_ptr(), _DTYPE[state.dtype], 0, state.shape[0])
+    return GdnStatePool(state.data_ptr(), _STATE_DTYPE[state.dtype], 0, state.shape[0])
+
+
+def cast_to_state(src: torch.Tensor, dtype: torch.dtype) -> torch.Tensor:
+    """fp32 device tensor -> a new tensor in a state format, rounded by the
+    library's store conversion (gdn_cast_to_state)."""
+    lib = load_library()
+    if src.dtype != torch.float32 or not src.is_contiguous():
+        raise ValueError("src must be a contiguous float32 tensor")
+    if dtype not in _STATE_DTYPE:
+        raise ValueError(f"{dtype} is not a state format")
+    dst = torch.empty(src.shape, dtype=dtype, device=src.device)
+    _check(lib.gdn_cast_to_state(_ptr(src), _ptr(dst), src.numel(), _STATE_DTYPE[dtype],
+                                 _stream(src.device)))
+    return dst
 
 
 def _stream(device) -> ctypes.c_void_p:

@@ -24,7 +24,8 @@ from typing import Optional
 import numpy as np
 import torch
 
-_DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+_DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
+       "f8": torch.float8_e4m3fn}
 
 
 @dataclass
@@ -223,6 +224,8 @@ CONFIGS = {
                        act="bf16", state="bf16", acc_lo=0, acc_hi=4, seed=4),
     "large_b512_f16": dict(kind="spec", B=512, T=8, HK=16, HV=32, act="bf16", state="f16",
                            acc_lo=1, acc_hi=8, seed=5),
+    "mtp_b128_f8": dict(kind="spec", B=128, T=8, HK=4, HV=32, act="bf16", state="f8",
+                        acc_lo=0, acc_hi=8, seed=3),
 }
 
 DESCRIPTIONS = {
@@ -235,6 +238,8 @@ DESCRIPTIONS = {
     "mixed_b128": "mixed batch: 64 non-spec T=1 + 64 spec T=4, HK=4 HV=32 K=V=128, bf16, "
                   "BF16 pool",
     "large_b512_f16": "decode B=512 T=8 HK=16 HV=32 K=V=128, bf16 activations, FP16 pool",
+    "mtp_b128_f8": "MTP decode B=128 T=8 HK=4 HV=32 K=V=128, bf16 activations, FP8 E4M3 pool, "
+                   "acc 0..8",
 }
 
 

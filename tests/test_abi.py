@@ -101,6 +101,7 @@ def test_valid_empty_batch_is_a_no_op(lib):
     (lambda L, P: (setattr(L, "num_k_heads", 2), setattr(L, "num_v_heads", 3)), 1, "multiple"),
     (lambda L, P: setattr(L, "num_k_heads", 0), 1, "positive"),
     (lambda L, P: setattr(L, "act_dtype", 7), 2, "act_dtype"),
+    (lambda L, P: setattr(L, "act_dtype", 3), 2, "act_dtype"),      # FP8 is a state format only
     (lambda L, P: setattr(L, "out_dtype", -1), 2, "out_dtype"),
     (lambda L, P: setattr(P, "dtype", 5), 2, "state dtype"),
     (lambda L, P: setattr(L.q, "data", None), 1, "q.data"),

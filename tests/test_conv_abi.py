@@ -62,6 +62,7 @@ def test_empty_batches_are_no_ops(lib):
     (lambda L, C: setattr(L, "width", 0), 1, "width"),
     (lambda L, C: setattr(L, "channels", 0), 1, "channels"),
     (lambda L, C: setattr(L, "x_dtype", 9), 2, "x_dtype"),
+    (lambda L, C: setattr(L, "x_dtype", 3), 2, "x_dtype"),        # FP8 is a state format only
     (lambda L, C: setattr(L, "out_dtype", -1), 2, "out_dtype"),
     (lambda L, C: setattr(L, "activation", 2), 1, "activation"),
     (lambda L, C: setattr(L, "weight", None), 1, "weight"),

@@ -26,6 +26,10 @@ from _helpers import bitwise_equal, rel_l2, slots_touched
 pytestmark = pytest.mark.gpu
 
 STATE_TOL = {torch.float32: 1e-5, torch.bfloat16: 3e-2, torch.float16: 3e-2}
+# FP8 E4M3 state: one unit in the last place -- spacing 2^-9 below 2^-6,
+# |x| 2^-3 above: a value the GPU (fp32) and the oracle (double) place on
+# opposite sides of a rounding boundary may land one step apart.
+F8_TOL = (2.0 ** -9, 2.0 ** -3)
 OUT_REL_L2 = 5e-4
 
 
@@ -98,10 +102,10 @@ def touched_slots_dev(before, after):
 
 
 def assert_state_close(g, o, dtype, what=""):
-    tol = STATE_TOL[dtype]
+    atol, rtol = F8_TOL if dtype == torch.float8_e4m3fn else (STATE_TOL[dtype],) * 2
     g = g.double().numpy()
     o = o.double().numpy()
-    err = np.abs(g - o) - (tol + tol * np.abs(o))
+    err = np.abs(g - o) - (atol + rtol * np.abs(o))
     assert np.all(np.isfinite(g)), f"{what}: non-finite state"
     assert err.max() <= 0, f"{what}: state mismatch, worst excess {err.max():.3e}"
 
@@ -485,3 +489,55 @@ def test_mixed_entry_with_one_part_empty(dev):
                            token_indx=a["non_spec_token_indx"], **common)
     torch.cuda.synchronize()
     assert torch.equal(st3, st4) and torch.equal(o3, o4)
+
+
+# --------------------------------------------------------------------------
+# FP8 E4M3 state (stores round to nearest even, saturating to +-448)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("HK,HV,act", [(1, 8, "bf16"), (2, 4, "f32")])
+def test_fp8_state(dev, HK, HV, act):
+    b = workloads.spec_batch(B=4, T=5, HK=HK, HV=HV, act=act, state="f8", q_lens=[5, 3, 0, 1],
+                             acc_lo=0, acc_hi=5, num_slots=24, seed=25)
+    check_full(b, dev)
+
+
+def test_fp8_state_mixed(dev):
+    b = workloads.mixed_batch(n_non_spec=6, n_spec=5, T=3, HK=1, HV=4, act="bf16", state="f8",
+                              seed=26)
+    check_full(b, dev)
+
+
+def test_fp8_full_size_sampled(dev):
+    check_sampled("mtp_b128_f8", dev)
+
+
+def test_fp8_state_saturates_and_keeps_nan(dev):
+    """Stores beyond the FP8 range saturate to +-448 and a NaN stays NaN, in
+    the token loop's encoder as in the oracle.  Values are scaled so that a
+    good share of every stored tile lands beyond 464 (where the bare
+    conversion gives a NaN code and the saturating re-encode must run), and
+    one v element is NaN, which makes one state row NaN from its token on."""
+    b = workloads.spec_batch(B=3, T=6, HK=1, HV=4, act="f32", state="f8", pool_std=120,
+                             acc_lo=1, acc_hi=6, seed=27)
+    b.pool = b.pool.float().nan_to_num(0.0).clamp(-448, 448).to(torch.float8_e4m3fn)
+    b.v = b.v * 5000.0
+    b.v[2, 1, 7] = float("nan")              # sequence 0, token 2, head 1, state row 7
+    pg, og = run_gpu(b, dev)
+    po, oo = run_oracle(b)
+    pg, og = pg.cpu(), og.cpu()
+    want = expected_slots(b)
+    g, o = pg[want].double(), po[want].double()
+    assert torch.equal(torch.isnan(g), torch.isnan(o))
+    nan = torch.isnan(o)
+    assert nan.any() and not nan.all()
+    sat = o.abs() == 448.0
+    assert sat.sum() > 1000, "the workload should saturate many stores"
+    assert torch.equal(g.abs() == 448.0, sat) or \
+        ((g.abs() == 448.0) != sat).sum() < 0.001 * sat.sum()   # ties at the edge only
+    err = (g - o).abs() - (F8_TOL[0] + F8_TOL[1] * o.abs())
+    assert err[~nan].max() <= 0
+    rows = processed_rows(b)
+    ogr, oor = og[rows].double(), oo[rows].double()
+    assert torch.equal(torch.isnan(ogr), torch.isnan(oor))
+    fin = ~torch.isnan(oor)
+    assert rel_l2(ogr[fin].numpy(), oor[fin].numpy()) < OUT_REL_L2

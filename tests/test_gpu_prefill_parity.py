@@ -20,6 +20,11 @@ from _helpers import rel_l2
 pytestmark = pytest.mark.gpu
 
 STATE_TOL = {torch.float32: 1e-5, torch.bfloat16: 3e-2, torch.float16: 3e-2}
+F8_TOL = (2.0 ** -9, 2.0 ** -3)      # one FP8 E4M3 step (see test_gpu_parity)
+
+
+def tols(dtype):
+    return F8_TOL if dtype == torch.float8_e4m3fn else (STATE_TOL[dtype],) * 2
 OUT_REL_L2 = 5e-4
 
 
@@ -69,14 +74,14 @@ def check(b, dev, **over):
     sentinel = torch.full((b.n_tok, b.HV, b.V), -5.0, dtype=b.out_dtype)
     gp, go = run_gpu(b, dev, out=sentinel, **over)
     op, oo = run_oracle(b, out=sentinel, **over)
-    tol = STATE_TOL[b.pool.dtype]
+    atol, rtol = tols(b.pool.dtype)
     si = over.get("state_indices", b.state_indices).tolist()
     cu = over.get("cu_seqlens", b.cu_seqlens).tolist()
     live = {s for i, s in enumerate(si) if s >= 0 and cu[i + 1] > cu[i]}
     for s in range(b.pool.shape[0]):
         if s in live:
             d = (gp[s].double() - op[s].double()).abs()
-            assert (d <= tol + tol * op[s].double().abs()).all(), (s, d.max())
+            assert (d <= atol + rtol * op[s].double().abs()).all(), (s, d.max())
         else:
             assert torch.equal(gp[s], b.pool[s]), f"slot {s} changed"
     rows = rows_of(b, over.get("cu_seqlens"), over.get("state_indices"), over.get("token_indx"))
@@ -92,7 +97,8 @@ def test_prefill_small(dev):
 
 
 @pytest.mark.parametrize("act,state,out", [("bf16", "f32", "bf16"), ("f32", "f32", "f32"),
-                                           ("bf16", "f16", "f32"), ("f16", "bf16", "f16")])
+                                           ("bf16", "f16", "f32"), ("f16", "bf16", "f16"),
+                                           ("bf16", "f8", "bf16")])
 def test_dtypes(dev, act, state, out):
     b = workloads.prefill_batch(lens=[45, 130, 9], HK=2, HV=4, act=act, state=state, out=out,
                                 chunk_size=16, init_frac=0.7, num_slots=5, seed=41)

@@ -23,7 +23,7 @@ from _helpers import (bitwise_equal, orc_decode, orc_spec, recover_o, rel_l2,
                       silu, slots_touched, tiny, with_pool_dtype)
 
 F64 = torch.float64
-DTYPES = [torch.float32, torch.bfloat16, torch.float16, torch.float64]
+DTYPES = [torch.float32, torch.bfloat16, torch.float16, torch.float64, torch.float8_e4m3fn]
 
 
 # --------------------------------------------------------------------------
@@ -66,6 +66,29 @@ def test_round_bf16_matches_torch():
     got = oracle.round_to(torch.bfloat16, x)
     ref = torch.from_numpy(x).to(torch.float32).to(torch.bfloat16).to(F64).numpy()
     assert np.array_equal(got, ref)
+
+
+def test_round_f8e4m3_matches_torch_in_range():
+    """Below the saturation point (464 = the tie between 448 and the NaN
+    code), torch's float8_e4m3fn conversion is one nearest-even rounding of
+    an exact fp32 value: the oracle must agree, subnormals and ties included."""
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal(6000) * np.exp2(rng.integers(-12, 9, 6000))
+    grid = np.array([m * 2.0 ** e for e in range(-9, 9) for m in range(8, 16)])
+    ties = np.concatenate([(grid[:-1] + grid[1:]) / 2, np.arange(1, 16) * 2.0 ** -10])
+    x = np.concatenate([x, ties, -ties, [447.9, 463.99, -463.99]])
+    x = x[np.abs(x) < 464].astype(np.float32).astype(np.float64)
+    got = oracle.round_to(torch.float8_e4m3fn, x)
+    ref = torch.from_numpy(x).to(torch.float32).to(torch.float8_e4m3fn).to(F64).numpy()
+    assert np.array_equal(got, ref)
+
+
+def test_round_f8e4m3_saturates():
+    """Reading: FP8 state stores saturate to +-448 (infinities included)
+    where torch's conversion produces NaN; NaN stays NaN."""
+    r = oracle.round_to(torch.float8_e4m3fn, [464.0, 1e6, -470.0, np.inf, -np.inf, 448.0])
+    assert list(r) == [448.0, 448.0, -448.0, 448.0, -448.0, 448.0]
+    assert np.isnan(oracle.round_to(torch.float8_e4m3fn, [np.nan])[0])
 
 
 def test_round_special_values():
