@@ -11,25 +11,33 @@
 // spelled out in gdn_conv.h.
 //
 // How it is computed here:
-//   * One 256-thread block per (sequence, block of channels).  In the fast
-//     path a thread owns a run of 8 channels, so every buffer position, input
-//     row and output row of the run is one 16-byte access per lane (two for
-//     fp32): a position-major buffer is read and written in coalesced 512 B
-//     rows.  A speculative block is 8 token slots x 32 runs (256 channels);
-//     a decode block is 256 runs (2048 channels).  A second instantiation
-//     takes one channel per thread with arbitrary strides (channel-major
-//     buffers, odd channel counts, unaligned views).
-//   * The block stages the window -- width - 1 history positions, then the
-//     draft inputs -- in LDS as fp32, each position loaded once; after one
+//   * Width 4 on the vector path (the conv width of the GDN layers, channel
+//     counts a multiple of 8, channel-contiguous buffer): one wave per
+//     (sequence, 512 channels), each lane a run of 8 channels, so every
+//     buffer position, input row and output row of the run is one 16-byte
+//     access per lane (two for fp32) and a wave moves coalesced 1 KiB rows.
+//     The wave issues every load of its window at once -- width - 1 history
+//     positions, then the draft inputs -- with the weights and bias of its
+//     channels, keeps the window in registers, writes the buffer back from
+//     the loaded bits and then computes and stores its outputs.  No LDS and
+//     no barrier: there is one round of load latency per wave, and with
+//     1,280 waves at the benchmark's shape every wave is resident at once.
+//     In-place safety: each buffer store waits for its own data, which was
+//     loaded after every history position that store may overwrite, and no
+//     two waves share a channel of a line.
+//   * Other widths and layouts (width 1-3, channel-major buffers, odd
+//     channel counts, unaligned views) take a block-staged kernel: one block
+//     per (sequence, block of channels) -- 8 token slots x 64 runs of 8
+//     channels, or one channel per thread with arbitrary strides -- stages
+//     the window in LDS as fp32, each position loaded once, and after one
 //     barrier each token slot computes its outputs from LDS and writes back
 //     its buffer positions.  All reads of a line precede the barrier and all
-//     writes follow it, and no two blocks share a channel of a line, so the
-//     in-place rewrite needs no other ordering.
-//   * Sequence metadata is block-uniform and read with scalar loads; a
-//     sequence with any out-of-range field is skipped by the whole block
-//     before anything is read or written.
-//   * The kernel is HBM-bound: per active sequence it reads width - 1
-//     history positions and L inputs and writes L outputs and width - 2 + L
+//     writes follow it.
+//   * Sequence metadata is uniform per wave and read with scalar loads; a
+//     sequence with any out-of-range field is skipped before anything is
+//     read or written.
+//   * The kernels are HBM-bound: per active sequence they read width - 1
+//     history positions and L inputs and write L outputs and width - 2 + L
 //     positions, about 4 flop per byte.  Buffer stores are non-temporal (the
 //     next read is one decode step away); output stores are not (the
 //     recurrent update reads them next).
@@ -385,12 +393,134 @@ __global__ void __launch_bounds__((Geo<SPEC, VEC>::THREADS)) conv_update_kernel(
                               y);
 }
 
+// Stores the raw bits of a run (a copy of loaded input bits), non-temporal
+// (vector path only).
+template <int DT, int EPT>
+__device__ __forceinline__ void store_raw_nt(char* b, const RawRun<DT, EPT>& r)
+{
+#pragma unroll
+    for (int c = 0; c < RawRun<DT, EPT>::CHUNKS; ++c) {
+        u32x4 w;
+        w[0] = r.d[4 * c]; w[1] = r.d[4 * c + 1]; w[2] = r.d[4 * c + 2]; w[3] = r.d[4 * c + 3];
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(b + 16 * c));
+    }
+}
+
+// Width-4 vector path: one wave per (entry, 512 channels).  Window slot s
+// holds window position s: slots 0..2 the history, slot 3 + t draft input t.
+template <int XT, int OT, bool SPEC>
+__global__ void __launch_bounds__(WAVE) conv_window_kernel(const ConvParams p)
+{
+    constexpr int NT = SPEC ? MAXT : 1;
+    constexpr int EPT = VEC_EPT;
+    constexpr int CB = WAVE * EPT;
+    constexpr int XSZ = XT == GDN_F32 ? 4 : 2;
+    constexpr int OSZ = OT == GDN_F32 ? 4 : 2;
+    constexpr int H = MAXW - 1;                     // history positions
+    const int r = static_cast<int>(threadIdx.x);
+    const int64_t seq = blockIdx.x / p.nblk;
+    const int64_t cbase = (blockIdx.x - seq * p.nblk) * static_cast<int64_t>(CB);
+    const int64_t c0 = cbase + static_cast<int64_t>(r) * EPT;
+
+    // ---- wave-uniform metadata, all loads first; one range predicate ----
+    const int64_t line = ro(p.lines)[seq];
+    int64_t first = seq;
+    int L = 1, a = 1;
+    if constexpr (SPEC) {
+        const int32_t lo = ro(p.cu)[seq], hi = ro(p.cu)[seq + 1];
+        a = ro(p.acc)[seq];
+        first = lo;
+        L = hi - lo;
+    }
+    const int64_t o = a > 1 ? a - 1 : 0;
+    if (!(line >= 0 && line < p.num_lines && first >= 0 && L >= 1 && L <= p.max_q_len &&
+          L <= NT && a >= 0 && o + H <= p.state_len && H - 1 + L <= p.state_len))
+        return;
+    int64_t rows[NT];
+    bool rows_ok = true;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+        const int64_t g = first + (i < L ? i : L - 1);
+        rows[i] = p.tix ? static_cast<int64_t>(ro(p.tix)[g]) : g;
+        rows_ok = rows_ok && rows[i] >= 0 && rows[i] < p.n_tok;
+    }
+    if (!rows_ok || c0 >= p.C)
+        return;
+
+    const uint32_t lane_x = static_cast<uint32_t>(r * EPT * XSZ);
+    const uint32_t lane_o = static_cast<uint32_t>(r * EPT * OSZ);
+    char* const cline = static_cast<char*>(p.cache) + (line * p.c_line + cbase) * XSZ + lane_x;
+
+    // ---- every load first: history, draft inputs, weights and bias ----
+    RawRun<XT, EPT> raw[H + NT];
+#pragma unroll
+    for (int q = 0; q < H; ++q)
+        load_raw<XT, EPT>(cline + (o + q) * p.c_pos * XSZ, raw[q]);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+        for (int i = 0; i < RawRun<XT, EPT>::N; ++i)
+            raw[H + t].d[i] = 0;
+        if (t < L)
+            load_raw<XT, EPT>(static_cast<const char*>(p.x) + (rows[t] * p.x_st + cbase) * XSZ +
+                                  lane_x, raw[H + t]);
+    }
+    float4 w4[EPT];
+    float bs[EPT];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+        w4[e] = reinterpret_cast<const float4*>(p.weight)[c0 + e];
+        bs[e] = 0.0f;
+    }
+    if (p.bias) {
+        const float4 b0 = reinterpret_cast<const float4*>(p.bias + c0)[0];
+        const float4 b1 = reinterpret_cast<const float4*>(p.bias + c0)[1];
+        bs[0] = b0.x; bs[1] = b0.y; bs[2] = b0.z; bs[3] = b0.w;
+        bs[4] = b1.x; bs[5] = b1.y; bs[6] = b1.z; bs[7] = b1.w;
+    }
+
+    // ---- write-back: position q <- slot q + 1 for q < H - 1 + L, as loaded ----
+#pragma unroll
+    for (int q = 0; q < H - 1 + NT; ++q)
+        if (q < H - 1 + L)
+            store_raw_nt<XT, EPT>(cline + q * p.c_pos * XSZ, raw[q + 1]);
+
+    // ---- outputs: taps in ascending order, one FMA each ----
+    float e[H + NT][EPT];
+#pragma unroll
+    for (int sl = 0; sl < H + NT; ++sl)
+        unpack_run<XT, EPT>(raw[sl], e[sl]);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        if (t < L) {
+            float y[EPT];
+#pragma unroll
+            for (int c = 0; c < EPT; ++c) {
+                float acc = bs[c];
+                acc = fmaf(w4[c].x, e[t][c], acc);
+                acc = fmaf(w4[c].y, e[t + 1][c], acc);
+                acc = fmaf(w4[c].z, e[t + 2][c], acc);
+                acc = fmaf(w4[c].w, e[t + 3][c], acc);
+                y[c] = p.act == GDN_CONV_ACT_SILU ? silu(acc) : acc;
+            }
+            store_run<OT, EPT, false>(
+                static_cast<char*>(p.out) + (rows[t] * p.o_st + cbase) * OSZ + lane_o, y);
+        }
+    }
+}
+
 template <int X, int O, bool SPEC>
 hipError_t launch_ept(const ConvParams& p, bool vec, hipStream_t s)
 {
-    const int64_t grid = static_cast<int64_t>(p.num_seqs) * p.nblk;
     ConvParams args = p;
     void* argv[] = {&args};
+    if (vec && p.W == MAXW) {
+        args.nblk = (p.C + WAVE * VEC_EPT - 1) / (WAVE * VEC_EPT);
+        const int64_t grid = static_cast<int64_t>(p.num_seqs) * args.nblk;
+        return hipLaunchKernel(reinterpret_cast<const void*>(&conv_window_kernel<X, O, SPEC>),
+                               dim3(static_cast<uint32_t>(grid)), dim3(WAVE), argv, 0, s);
+    }
+    const int64_t grid = static_cast<int64_t>(p.num_seqs) * p.nblk;
     const void* fn = vec ? reinterpret_cast<const void*>(&conv_update_kernel<X, O, SPEC, true>)
                          : reinterpret_cast<const void*>(&conv_update_kernel<X, O, SPEC, false>);
     const int threads = vec ? Geo<SPEC, true>::THREADS : Geo<SPEC, false>::THREADS;
