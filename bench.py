@@ -77,37 +77,65 @@ def recorded_traffic(workload: str, path: str = "gdn"):
     return entry.get("bytes_per_launch")
 
 
-def cpu_baseline(batch, n_seqs: int):
-    """The oracle, as it is, on the first n_seqs sequences of the workload."""
-    import numpy as np
+def _oracle_subset(batch, lo: int, hi: int):
+    """Positional and keyword arguments of oracle.spec_update for sequences
+    lo..hi-1 of the workload, on their own rows and a pool of just the slots
+    they touch."""
     import torch
 
-    import oracle
-
     cu = batch.cu_seqlens.tolist()
-    rows = list(range(cu[0], cu[n_seqs]))
+    rows = list(range(cu[lo], cu[hi]))
     slots = set()
-    for bi in range(n_seqs):
+    for bi in range(lo, hi):
         acc = int(batch.num_accepted_tokens[bi])
         slots.add(int(batch.spec_state_indices[bi, max(acc - 1, 0)]))
         slots |= set(batch.spec_state_indices[bi].tolist())
     slots = sorted(slots)
     remap = {s: i for i, s in enumerate(slots)}
     si = torch.tensor([[remap[int(s)] for s in batch.spec_state_indices[bi]]
-                       for bi in range(n_seqs)], dtype=torch.int32)
+                       for bi in range(lo, hi)], dtype=torch.int32)
     sub = [x[rows] for x in (batch.q, batch.k, batch.v, batch.z, batch.a, batch.b)]
-    pool = batch.pool[slots]
+    args = sub + [batch.A_log, batch.dt_bias, batch.norm_weight, batch.pool[slots],
+                  batch.cu_seqlens[lo: hi + 1] - cu[lo], si, batch.num_accepted_tokens[lo:hi]]
+    kw = dict(out_dtype=batch.out_dtype, scale=batch.scale, norm_eps=batch.norm_eps)
+    return args, kw, len(rows)
+
+
+def cpu_baseline(batch, n_seqs: int):
+    """The oracle, as it is, on the first n_seqs sequences of the workload."""
+    import oracle
+
+    args, kw, tokens = _oracle_subset(batch, 0, n_seqs)
     t0 = time.perf_counter()
-    oracle.spec_update(*sub, batch.A_log, batch.dt_bias, batch.norm_weight, pool,
-                       batch.cu_seqlens[: n_seqs + 1], si,
-                       batch.num_accepted_tokens[:n_seqs], out_dtype=batch.out_dtype,
-                       scale=batch.scale, norm_eps=batch.norm_eps)
+    oracle.spec_update(*args, **kw)
     dt = time.perf_counter() - t0
-    tokens = len(rows)
     return {"value": tokens / dt, "unit": "draft tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"first {n_seqs} of {batch.num_seqs} sequences ({tokens} draft tokens, "
                       f"all {batch.HV} v-heads) of the same workload; serial C, float64; "
                       f"{dt:.2f} s incl. fp64 marshalling"}
+
+
+def cpu_baseline_threads(batch, n_seqs: int, threads: int):
+    """The same oracle on the same sample, its sequences split into `threads`
+    contiguous parts run at once on host threads (one oracle call per part;
+    the calls share nothing, and ctypes releases the interpreter lock while
+    the C code runs)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+
+    threads = max(1, min(threads, n_seqs))
+    bounds = [n_seqs * i // threads for i in range(threads + 1)]
+    parts = [_oracle_subset(batch, bounds[i], bounds[i + 1]) for i in range(threads)]
+    oracle.round_to(batch.pool.dtype, [0.0])              # load the library before timing
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(lambda a: oracle.spec_update(*a[0], **a[1]), parts))
+    dt = time.perf_counter() - t0
+    tokens = sum(x[2] for x in parts)
+    return {"value": tokens / dt, "unit": "draft tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n_seqs} of {batch.num_seqs} sequences ({tokens} draft tokens) "
+                      f"in {threads} parts on {threads} host threads; {dt:.2f} s"}
 
 
 def conv_cpu_baseline(batch):
@@ -211,6 +239,9 @@ def main():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run --steps plain device copies of MIB "
                          "MiB each (reference kernel for scaling HBM byte counters)")
+    ap.add_argument("--cpu-threads", type=int,
+                    default=min(16, len(os.sched_getaffinity(0))),
+                    help="host threads for the multi-threaded oracle timing (gdn path)")
     ap.add_argument("--cpu-seqs", type=int, default=128,
                     help="sequences of the workload the CPU oracle is timed on (0: skip)")
     args = ap.parse_args()
@@ -264,7 +295,11 @@ def main():
     achieved = alg_bytes / (avg_ms * 1e-3) / 1e9
     traffic = recorded_traffic(args.workload, "gdn")
     ms_per_step = gpu_ms / args.steps
-    cpu = cpu_baseline(batch, min(args.cpu_seqs, batch.num_seqs)) if args.cpu_seqs > 0 else None
+    cpu = cpu_all = None
+    if args.cpu_seqs > 0:
+        n = min(args.cpu_seqs, batch.num_seqs)
+        cpu = cpu_baseline(batch, n)
+        cpu_all = cpu_baseline_threads(batch, n, args.cpu_threads)
     dtypes = {torch.float32: "f32", torch.bfloat16: "bf16", torch.float16: "f16",
               torch.float8_e4m3fn: "f8e4m3"}
     line = {
@@ -290,6 +325,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic, **tf},
         "cpu_baseline": cpu,
+        "cpu_baseline_threads": cpu_all,
     }
     print(json.dumps(line), flush=True)
 

@@ -21,7 +21,7 @@
 //     channels, keeps the window in registers, writes the buffer back from
 //     the loaded bits and then computes and stores its outputs.  No LDS and
 //     no barrier: there is one round of load latency per wave, and with
-//     1,280 waves at the benchmark's shape every wave is resident at once.
+//     1,280 waves at B = 128, C = 5120 every wave is resident at once.
 //     In-place safety: each buffer store waits for its own data, which was
 //     loaded after every history position that store may overwrite, and no
 //     two waves share a channel of a line.
