@@ -213,3 +213,23 @@ def test_full_size_element_wise_path(dev):
     """The full batch with a channel count that forces the element-wise path."""
     b = workloads.make_conv("conv_mtp_b128", C=5120 + 4, seed=12)
     check(b, dev)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_entry_gathered(dev, dtype):
+    """The decode entry with a gather index: entry i reads row token_indx[i]
+    and writes its output to that row."""
+    C, W, n = 512, 4, 24
+    b = workloads.conv_batch(B=n, T=1, C=C, width=W, dtype=dtype, state_len=W - 1,
+                             num_lines=n + 2, seed=62)
+    perm = torch.from_numpy(np.random.default_rng(62).permutation(n).astype(np.int32))
+    x, cache = b.x.to(dev), b.cache.to(dev).clone()
+    out = torch.full(x.shape, 3.0, dtype=x.dtype, device=dev)
+    ops.conv_decode_update(x, b.weight.to(dev), b.bias.to(dev), cache, b.conv_indices.to(dev),
+                           token_indx=perm.to(dev), out=out)
+    torch.cuda.synchronize()
+    oc, oo = oracle.conv_decode_update(b.x, b.weight, b.bias, b.cache, b.conv_indices,
+                                       token_indx=perm, out=torch.full(b.x.shape, 3.0,
+                                                                        dtype=b.x.dtype))
+    assert torch.equal(cache.cpu(), oc)
+    assert_out_close(out.cpu(), oo, list(range(n)), b.out_dtype)
