@@ -118,13 +118,16 @@ gdn_update_kernel(const KParams p)
     // b % 8).  Give each XCD one contiguous range of units instead, so the
     // heads of a sequence -- whose state tiles are adjacent in a slot and whose
     // q/k rows are shared -- meet in one XCD's L2.  Bijective for any grid.
-    const int64_t nblk = gridDim.x;
-    const int64_t xcd = blockIdx.x % NXCD;
-    const int64_t per = nblk / NXCD, rem = nblk % NXCD;
-    const int64_t unit = xcd * per + (xcd < rem ? xcd : rem) + blockIdx.x / NXCD;
-    const int64_t entry = unit / p.HV;
-    const int h = static_cast<int>(unit - entry * p.HV);
-    const int kh = h / p.group;
+    // Grid and head counts fit 32 bits (the host checks units < 2^31), so
+    // the unit arithmetic stays 32-bit: no 64-bit division in the prologue.
+    const uint32_t nblk = gridDim.x;
+    const uint32_t xcd = blockIdx.x % NXCD;
+    const uint32_t per = nblk / NXCD, rem = nblk % NXCD;
+    const uint32_t unit = xcd * per + (xcd < rem ? xcd : rem) + blockIdx.x / NXCD;
+    const uint32_t entry32 = unit / static_cast<uint32_t>(p.HV);
+    const int64_t entry = entry32;
+    const int h = static_cast<int>(unit - entry32 * static_cast<uint32_t>(p.HV));
+    const int kh = static_cast<int>(static_cast<uint32_t>(h) / static_cast<uint32_t>(p.group));
 
     // A mixed launch interleaves its two kinds of entries in proportion, so
     // that every XCD's contiguous range gets its share of the heavier spec
@@ -228,8 +231,8 @@ gdn_update_kernel(const KParams p)
         const float2 kv = unpack_pair<ACT>(kr[i]);
         const float nq = sum64(qv.x * qv.x + qv.y * qv.y);
         const float nk = sum64(kv.x * kv.x + kv.y * kv.y);
-        const float rk = 1.0f / sqrtf(nk + 1e-6f);
-        const float rq = p.scale / sqrtf(nq + 1e-6f);
+        const float rk = frsqrt(nk + 1e-6f);
+        const float rq = p.scale * frsqrt(nq + 1e-6f);
         const float2 kn = make_float2(kv.x * rk, kv.y * rk);
         const float2 qn = make_float2(qv.x * rq, qv.y * rq);
         const float kq = sum64(kn.x * qn.x + kn.y * qn.y);
@@ -241,9 +244,8 @@ gdn_update_kernel(const KParams p)
             if (lane == 0) {
                 sRow[t] = rowv[i];
                 const float x = unpack_one<ACT>(ar[i]) + dtb;
-                const float sp = x > 20.0f ? x : log1pf(expf(x));
-                sAlpha[t] = expf(A * sp);
-                sBeta[t] = 1.0f / (1.0f + expf(-unpack_one<ACT>(br[i])));
+                sAlpha[t] = fexp(A * softplus_fast(x));
+                sBeta[t] = sigmoid_fast(unpack_one<ACT>(br[i]));
                 sKQ[t] = kq;
             }
         }
@@ -342,9 +344,9 @@ gdn_update_kernel(const KParams p)
             const float2 zv = *reinterpret_cast<const float2*>(&sZ[t][2 * el]);
             const int64_t row = sRow[t];
             const float ms = sum64(o.x * o.x + o.y * o.y) * (1.0f / D);
-            const float rr = 1.0f / sqrtf(ms + p.norm_eps);
-            const float gx = zv.x / (1.0f + expf(-zv.x));
-            const float gy = zv.y / (1.0f + expf(-zv.y));
+            const float rr = frsqrt(ms + p.norm_eps);
+            const float gx = zv.x * sigmoid_fast(zv.x);
+            const float gy = zv.y * sigmoid_fast(zv.y);
             const float2 y = make_float2(o.x * rr * wn.x * gx, o.y * rr * wn.y * gy);
             store_pair<OUT>(p.out, row * p.o_st + h * p.o_sh + 2 * el, y);
         }

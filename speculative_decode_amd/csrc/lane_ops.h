@@ -1,5 +1,6 @@
 // lane_ops.h -- cross-lane sums over 8-lane row groups and over a wave64,
-// built from DPP row operations, shared by the HIP kernels.
+// built from DPP row operations, and the scalar math of the per-token gates,
+// norms and gated RMSNorm, shared by the HIP kernels.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -34,5 +35,34 @@ __device__ __forceinline__ float sum64(float x)
     const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
     return (r0 + r1) + (r2 + r3);
 }
+
+// Per-token scalar math on the hardware transcendental units: v_exp_f32 and
+// v_log_f32 (base 2), v_rcp_f32 and v_rsq_f32, each within about one ulp.
+// They replace the correctly rounded library sequences, which cost tens of
+// instructions each, in the prologue and epilogue of every unit; the
+// resulting differences (order 1e-7 relative) are far inside the parity
+// bars.  Limits: fexp(-inf) = 0, fexp(+inf) = +inf, frcp(+inf) = 0.
+__device__ __forceinline__ float fexp(float x)
+{
+    return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+}
+
+__device__ __forceinline__ float flog(float x)
+{
+    return __builtin_amdgcn_logf(x) * 0.6931471805599453f;
+}
+
+__device__ __forceinline__ float frcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+__device__ __forceinline__ float frsqrt(float x) { return __builtin_amdgcn_rsqf(x); }
+
+// softplus(x) = log(1 + e^x), linear above 20; for very negative x the sum
+// 1 + e^x rounds, an absolute error below 2^-24.
+__device__ __forceinline__ float softplus_fast(float x)
+{
+    return x > 20.0f ? x : flog(1.0f + fexp(x));
+}
+
+__device__ __forceinline__ float sigmoid_fast(float x) { return frcp(1.0f + fexp(-x)); }
 
 }  // namespace gdn_dev

@@ -135,13 +135,14 @@ gdn_prefill_kernel(const PParams p)
     const int j = lane & 7;
 
     // XCD-contiguous units: the heads of a sequence share its q/k rows.
-    const int64_t nblk = gridDim.x;
-    const int64_t xcd = blockIdx.x % NXCD;
-    const int64_t per = nblk / NXCD, rem = nblk % NXCD;
-    const int64_t unit = xcd * per + (xcd < rem ? xcd : rem) + blockIdx.x / NXCD;
-    const int64_t seq = unit / p.HV;
-    const int h = static_cast<int>(unit - seq * p.HV);
-    const int kh = h / p.group;
+    const uint32_t nblk = gridDim.x;
+    const uint32_t xcd = blockIdx.x % NXCD;
+    const uint32_t per = nblk / NXCD, rem = nblk % NXCD;
+    const uint32_t unit = xcd * per + (xcd < rem ? xcd : rem) + blockIdx.x / NXCD;
+    const uint32_t seq32 = unit / static_cast<uint32_t>(p.HV);
+    const int64_t seq = seq32;
+    const int h = static_cast<int>(unit - seq32 * static_cast<uint32_t>(p.HV));
+    const int kh = static_cast<int>(static_cast<uint32_t>(h) / static_cast<uint32_t>(p.group));
 
     // ---- metadata; a sequence with any out-of-range field is skipped whole ----
     const int64_t c0 = p.cu[seq];
@@ -196,8 +197,8 @@ gdn_prefill_kernel(const PParams p)
             const float2 kv = unpack_pair<ACT>(raw.k[i]);
             const float nq = sum64(qv.x * qv.x + qv.y * qv.y);
             const float nk = sum64(kv.x * kv.x + kv.y * kv.y);
-            const float rk = 1.0f / sqrtf(nk + 1e-6f);
-            const float rq = p.scale / sqrtf(nq + 1e-6f);
+            const float rk = frsqrt(nk + 1e-6f);
+            const float rq = p.scale * frsqrt(nq + 1e-6f);
             const float2 kn = make_float2(kv.x * rk, kv.y * rk);
             const float2 qn = make_float2(qv.x * rq, qv.y * rq);
             const float kq = sum64(kn.x * qn.x + kn.y * qn.y);
@@ -209,9 +210,8 @@ gdn_prefill_kernel(const PParams p)
                 if (lane == 0) {
                     B.row[tl] = raw.row[i];
                     const float x = unpack_one<ACT>(raw.a[i]) + dtb;
-                    const float sp = x > 20.0f ? x : log1pf(expf(x));
-                    B.alpha[tl] = expf(A * sp);
-                    B.beta[tl] = 1.0f / (1.0f + expf(-unpack_one<ACT>(raw.b[i])));
+                    B.alpha[tl] = fexp(A * softplus_fast(x));
+                    B.beta[tl] = sigmoid_fast(unpack_one<ACT>(raw.b[i]));
                     B.kq[tl] = kq;
                 }
             }
@@ -281,9 +281,9 @@ gdn_prefill_kernel(const PParams p)
                 const float2 zv = *reinterpret_cast<const float2*>(&B.z[tl][2 * lane]);
                 const int64_t row = B.row[tl];
                 const float ms = sum64(o.x * o.x + o.y * o.y) * (1.0f / D);
-                const float rr = 1.0f / sqrtf(ms + p.norm_eps);
-                const float gx = zv.x / (1.0f + expf(-zv.x));
-                const float gy = zv.y / (1.0f + expf(-zv.y));
+                const float rr = frsqrt(ms + p.norm_eps);
+                const float gx = zv.x * sigmoid_fast(zv.x);
+                const float gy = zv.y * sigmoid_fast(zv.y);
                 const float2 y = make_float2(o.x * rr * wn.x * gx, o.y * rr * wn.y * gy);
                 store_pair<OUT>(p.out, row * p.o_st + h * p.o_sh + 2 * lane, y);
             }
