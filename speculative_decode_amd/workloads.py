@@ -226,6 +226,8 @@ CONFIGS = {
                            acc_lo=1, acc_hi=8, seed=5),
     "mtp_b128_f8": dict(kind="spec", B=128, T=8, HK=4, HV=32, act="bf16", state="f8",
                         acc_lo=0, acc_hi=8, seed=3),
+    "decode_b128": dict(kind="mixed", n_non_spec=128, n_spec=0, T=1, HK=4, HV=32,
+                        act="bf16", state="bf16", seed=6),
 }
 
 DESCRIPTIONS = {
@@ -240,6 +242,8 @@ DESCRIPTIONS = {
     "large_b512_f16": "decode B=512 T=8 HK=16 HV=32 K=V=128, bf16 activations, FP16 pool",
     "mtp_b128_f8": "MTP decode B=128 T=8 HK=4 HV=32 K=V=128, bf16 activations, FP8 E4M3 pool, "
                    "acc 0..8",
+    "decode_b128": "non-spec decode B=128 (one token each, slots updated in place) HK=4 HV=32 "
+                   "K=V=128, bf16 activations, BF16 pool",
 }
 
 
