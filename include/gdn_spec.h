@@ -34,7 +34,9 @@
  *     out[row][h] = o / sqrt(mean(o^2) + norm_eps) * norm_weight * silu(z[row][h])
  *   with kh = h / (HV / HK).  The FP32 carry S is not re-rounded between
  *   tokens; rounding happens only at the slot and output stores (to nearest,
- *   ties to even).
+ *   ties to even).  The arithmetic is FP32; exp, log, the reciprocals and
+ *   the reciprocal square roots of the gates, norms and RMSNorm come from the
+ *   hardware units, each within about one ulp.
  *
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers, owned by the caller.  The
