@@ -1,5 +1,6 @@
 // gdn_kernels.hip -- fused Gated DeltaNet speculative-decode state update for
-// CDNA4 (gfx950), and the two C-ABI launch entry points.
+// CDNA4 (gfx950), and its C-ABI entry points (speculative, single-token,
+// mixed, and the state-format cast).
 //
 // What is computed is fixed by the vLLM PR reports on prhub.com.cn (#51674
 // 实现拆解 item 1: one block per (request, value head), rewind by
@@ -12,7 +13,8 @@
 //   * One 256-thread workgroup (4 wave64) per (sequence, value head); a 1-D
 //     grid of num_seqs*HV workgroups, mapped so each XCD works on a
 //     contiguous range of units.  Batches above one round of resident
-//     blocks run one block per CU (an LDS reservation caps occupancy).
+//     blocks are capped by an LDS reservation: one block per CU for 7-8
+//     draft tokens, two for 2-6, none for single tokens or an FP8 pool.
 //   * The 128x128 state tile (V rows, K contiguous) lives in registers for
 //     the whole draft: each 8-lane group owns one row at a time, each lane 16
 //     of its elements, and every lane holds 4 rows (64 fp32 values).  A row
@@ -28,7 +30,8 @@
 //     which is S_t q^ of the updated state without a second pass.
 //   * Per-token vectors (k^, q^, v) and scalars (alpha, beta, k^.q^) are
 //     computed once per workgroup in a prologue and shared through LDS; the
-//     read-outs o go to LDS for the per-(token, head) RMSNorm epilogue.
+//     read-outs o go to LDS for the per-(token, head) RMSNorm epilogue.  The
+//     scalar math of both uses the hardware exp/log/rcp/rsq units.
 //   * No MFMA: a rank-1 recurrence is not a dense contraction.  The kernel is
 //     bound by HBM bandwidth (8 of 9 tile transfers at T=8 are stores).
 #include <hip/hip_runtime.h>

@@ -22,10 +22,12 @@
 //     step's activation loads are issued before this step's token loop, so
 //     their latency hides behind the recurrence.
 //   * Why not the chunkwise (WY / UT-transform) form: it trades the serial
-//     recurrence for dense C x C, C x K and K x V products per chunk -- more
-//     arithmetic in total -- to run them on matrix cores.  On MI355X the
-//     FP32 matrix rate equals the FP32 vector rate, and the pages fix FP32
-//     arithmetic, so the chunkwise form would do more work at the same peak.
+//     recurrence for dense C x C, C x K and K x V products per chunk -- about
+//     1.6x the arithmetic at C = 64, plus a triangular solve -- to run them on
+//     matrix cores.  The pages fix FP32 arithmetic.  The FP32 matrix rate of
+//     MI355X is twice the non-packed vector rate this kernel issues at, so
+//     even small products running at the matrix peak would gain at most
+//     about 1.25x; BF16 matrix operands would give up the FP32 arithmetic.
 //   * Prefill is compute-bound (about 130 flop per byte of HBM traffic): the
 //     roofline is the FP32 vector ALU.
 #include <hip/hip_runtime.h>
