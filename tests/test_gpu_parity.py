@@ -541,3 +541,32 @@ def test_fp8_state_saturates_and_keeps_nan(dev):
     assert torch.equal(torch.isnan(ogr), torch.isnan(oor))
     fin = ~torch.isnan(oor)
     assert rel_l2(ogr[fin].numpy(), oor[fin].numpy()) < OUT_REL_L2
+
+
+def _random_config(i):
+    """Configuration i of the randomized sweep (a fixed generator: the same
+    twenty configurations every run)."""
+    r = np.random.default_rng(1000 + i)
+    HK = int(r.choice([1, 2, 4]))
+    HV = HK * int(r.choice([1, 2, 4, 8]))
+    B = int(r.integers(1, 7))
+    T = int(r.integers(1, 9))
+    q_lens = [int(x) for x in r.integers(0, T + 1, size=B)]
+    if sum(q_lens) == 0:
+        q_lens[0] = T
+    dts = ["f32", "bf16", "f16"]
+    return dict(B=B, T=T, HK=HK, HV=HV, act=str(r.choice(dts)),
+                state=str(r.choice(dts + ["f8"])), out=str(r.choice(dts)), q_lens=q_lens,
+                acc_lo=0, acc_hi=T, num_slots=B * T + int(r.integers(0, 5)), seed=2000 + i), r
+
+
+@pytest.mark.parametrize("i", range(20))
+def test_random_configurations(dev, i):
+    """Twenty seeded random shapes, dtypes, ragged lengths, acceptances, pool
+    sizes and (for some) a permuted gather index, each compared whole."""
+    cfg, r = _random_config(i)
+    b = workloads.spec_batch(**cfg)
+    if r.random() < 0.5 and b.n_tok > 1:
+        perm = r.permutation(b.n_tok).astype(np.int32)
+        b.spec_token_indx = torch.from_numpy(perm)
+    check_full(b, dev)
