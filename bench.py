@@ -7,8 +7,9 @@ One step = one launch of the whole hot path (rewind, gating, L2 norms, the
 serial recurrence over the draft tokens, every slot store, the gated-RMSNorm
 epilogue) over one batch of synthetic inputs already resident in HBM.  Steps
 run back to back on torch's current stream and cycle through the state pools
-of --layers GDN layers (4 by default), as a decode step walks a model's
-layers: the pools together are several times the 256 MB Infinity Cache, so a
+of --layers GDN layers (by default 4, or more for small pools so that they
+total at least 2 GiB), as a decode step walks a model's layers: the pools
+together are several times the 256 MB Infinity Cache, so a
 step cannot find the slots it rewrites still cached from the step before.
 Every pool is updated in place.
 
@@ -44,6 +45,10 @@ PEAK_FP32_TFLOPS = 157.3       # MI355X FP32 vector, AMD's published figure
 DEFAULT_WORKLOAD = {"gdn": "mtp_b128_bf16", "conv": "conv_mtp_b128",
                     "prefill": "prefill_b16_l2048"}
 DEFAULT_LAYERS = {"gdn": 4, "conv": 32, "prefill": 2}
+# The state pools cycled by the gdn path must together be several times the
+# 256 MB Infinity Cache, else a step's rewind reads find slots written a few
+# steps earlier still cached: at least 4 pools and at least 2 GiB in all.
+MIN_CYCLED_POOL_BYTES = 2 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 _CSRC = os.path.join(ROOT, "speculative_decode_amd", "csrc")
 KERNEL_SOURCES = {
@@ -234,8 +239,9 @@ def main():
                          "with rewind that precedes it; prefill: the chunked prefill")
     ap.add_argument("--workload", default=None)
     ap.add_argument("--layers", type=int, default=None,
-                    help="layers cycled through, each with its own state (default 4 for "
-                         "gdn, 32 for conv)")
+                    help="layers cycled through, each with its own state (default: for "
+                         "gdn 4, or as many as make 2 GiB of pools; 32 for conv; 2 for "
+                         "prefill)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run --steps plain device copies of MIB "
                          "MiB each (reference kernel for scaling HBM byte counters)")
@@ -268,6 +274,7 @@ def main():
         return
     ops.load_library()
     args.workload = args.workload or DEFAULT_WORKLOAD[args.path]
+    layers_given = args.layers
     args.layers = args.layers or DEFAULT_LAYERS[args.path]
     if args.path == "conv":
         return bench_conv(args, dev)
@@ -278,6 +285,9 @@ def main():
           flush=True)
     kw = ops.batch_args(batch, dev)
     kw["out"] = torch.zeros((batch.n_tok, batch.HV, batch.V), dtype=batch.out_dtype, device=dev)
+    pool_bytes = batch.pool.numel() * batch.pool.element_size()
+    if not layers_given:
+        args.layers = max(args.layers, -(-MIN_CYCLED_POOL_BYTES // pool_bytes))
     pools = [kw["state"]] + [kw["state"].clone() for _ in range(args.layers - 1)]
     tokens = batch.draft_tokens()
     alg_bytes = batch.algorithmic_bytes()
@@ -321,7 +331,7 @@ def main():
                    "HK": batch.HK, "HV": batch.HV, "K": batch.K, "V": batch.V,
                    "act_dtype": dtypes[batch.q.dtype], "state_dtype": dtypes[batch.pool.dtype],
                    "algorithmic_bytes_per_step": alg_bytes, "layers_cycled": len(pools),
-                   "pool_bytes_per_layer": batch.pool.numel() * batch.pool.element_size()},
+                   "pool_bytes_per_layer": pool_bytes},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic, **tf},
         "cpu_baseline": cpu,

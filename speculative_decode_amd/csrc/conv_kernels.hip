@@ -112,7 +112,10 @@ __device__ __forceinline__ void load_raw(const char* b, RawRun<DT, EPT>& r)
     } else {
 #pragma unroll
         for (int c = 0; c < RawRun<DT, EPT>::CHUNKS; ++c) {
-            const uint4 a = *reinterpret_cast<const uint4*>(b + 16 * c);
+            // Streaming (non-temporal) loads: each run is read once per
+            // launch, and buffer positions are rewritten in place right after.
+            const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(b + 16 * c));
+            const uint4 a = make_uint4(v[0], v[1], v[2], v[3]);
             r.d[4 * c] = a.x; r.d[4 * c + 1] = a.y; r.d[4 * c + 2] = a.z; r.d[4 * c + 3] = a.w;
         }
     }

@@ -12,16 +12,16 @@
 // How it is computed here (not the pages' CUDA design):
 //   * One 256-thread workgroup (4 wave64) per (sequence, value head); a 1-D
 //     grid of num_seqs*HV workgroups, mapped so each XCD works on a
-//     contiguous range of units.  Batches above one round of resident
-//     blocks are capped by an LDS reservation: one block per CU for 7-8
-//     draft tokens, two for 2-6, none for single tokens or an FP8 pool.
+//     contiguous range of units.  Launches are capped by an LDS
+//     reservation: one block per CU for 7-8 draft tokens, two for 2-6, none
+//     for single tokens or an FP8 pool.
 //   * The 128x128 state tile (V rows, K contiguous) lives in registers for
 //     the whole draft: each 8-lane group owns one row at a time, each lane 16
 //     of its elements, and every lane holds 4 rows (64 fp32 values).  A row
 //     chunk moves as one 16-byte access per lane, so one wave instruction
 //     covers eight full 128-byte lines.  The tile is read from HBM once and
-//     written once per draft token with non-temporal stores; nothing else
-//     touches it.
+//     written once per draft token, both with non-temporal accesses; nothing
+//     else touches it.
 //   * Rows of S evolve independently.  Per token and row, the two dot
 //     products of the OLD row (S.k^ and S.q^) are reduced together over the
 //     8 lanes with three DPP steps; then
@@ -210,7 +210,10 @@ gdn_update_kernel(const KParams p)
     const float A = -expf(p.A_log[h]);
     const float dtb = p.dt_bias[h];
 
-    // ---- the rewind tile: read once, 16 B per lane per chunk ----
+    // ---- the rewind tile: read once, 16 B per lane per chunk.  Streaming
+    // (non-temporal) loads: nothing reads the tile again in this launch, and
+    // a single-token unit rewrites these very lines, which then find no copy
+    // of them in L2 to update. ----
     const size_t tile = static_cast<size_t>(D) * D;
     const char* rbase = static_cast<const char*>(p.pool) +
                         (static_cast<size_t>(rslot) * p.HV + h) * tile * ESZ;
@@ -219,9 +222,11 @@ gdn_update_kernel(const KParams p)
     for (int r = 0; r < RPT; ++r) {
         const int row = wave * ROWS_PER_WAVE + r * 8 + g;
 #pragma unroll
-        for (int c = 0; c < CH; ++c)
-            raw[r][c] = *reinterpret_cast<const uint4*>(
-                rbase + (static_cast<size_t>(row) * D + c * CSTRIDE + j * EPC) * ESZ);
+        for (int c = 0; c < CH; ++c) {
+            const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+                rbase + (static_cast<size_t>(row) * D + c * CSTRIDE + j * EPC) * ESZ));
+            raw[r][c] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
     }
 
     // ---- prologue compute: gates, normalised k and q, k^.q^.  Everything
@@ -399,10 +404,7 @@ constexpr size_t static_lds_bytes(int nt)
            size_t(nt) * sizeof(int64_t);
 }
 
-// Blocks resident per CU before a batch counts as large.
-constexpr int ROUND_BLOCKS_PER_CU = 4;
-
-// Concurrent blocks per CU for a large batch whose units write up to
+// Concurrent blocks per CU for a launch whose units write up to
 // `writes` state tiles each (0: no cap).  A unit reads one tile and writes up
 // to `writes`.  With many such write streams per CU, the chip's writes land
 // on more DRAM rows at once than the memory keeps open, and the sustained
@@ -419,14 +421,14 @@ int blocks_per_cu_for(int writes, int state_dtype)
     return writes <= 6 ? 2 : 1;
 }
 
-// Dynamic LDS to reserve for a launch of nunits blocks.  Once a batch is
-// larger than one round of resident blocks, the launch reserves LDS that the
+// Dynamic LDS to reserve for a launch.  The launch reserves LDS that the
 // kernel never touches -- just over 1/(n+1) of a CU's, counting the static
 // LDS -- so that at most n blocks run per CU (n from blocks_per_cu_for).  The
 // stores of a finishing block still drain while the CU's next block loads.
-// A smaller batch keeps every unit resident at once.
+// The cap holds for small batches too: even a batch that would fit in one
+// round of resident blocks runs faster with fewer concurrent write streams.
 template <int NT>
-hipError_t plan_lds(int64_t nunits, int writes, int state_dtype, size_t* lds)
+hipError_t plan_lds(int writes, int state_dtype, size_t* lds)
 {
     *lds = 0;
     const int n = blocks_per_cu_for(writes, state_dtype);
@@ -436,8 +438,6 @@ hipError_t plan_lds(int64_t nunits, int writes, int state_dtype, size_t* lds)
     hipError_t e = device_info(&d);
     if (e != hipSuccess)
         return e;
-    if (nunits <= static_cast<int64_t>(d.cus) * ROUND_BLOCKS_PER_CU)
-        return hipSuccess;
     const size_t share = static_cast<size_t>(d.lds_per_cu) / (n + 1) + 1;
     if (share > static_lds_bytes(NT) && share <= static_cast<size_t>(d.lds_per_block))
         *lds = share - static_lds_bytes(NT);
@@ -448,7 +448,7 @@ template <int A, int S, int O, bool SPEC>
 hipError_t launch_typed(const KParams& p, int64_t grid, hipStream_t stream)
 {
     size_t lds = 0;
-    hipError_t e = plan_lds<SPEC ? MAXT : 1>(grid, p.max_writes, S, &lds);
+    hipError_t e = plan_lds<SPEC ? MAXT : 1>(p.max_writes, S, &lds);
     if (e != hipSuccess)
         return e;
     KParams args = p;

@@ -399,8 +399,9 @@ def test_full_size_sampled(dev, name):
 
 
 # --------------------------------------------------------------------------
-# batches above one round of resident blocks launch with an LDS reservation
-# that holds one block per CU; ragged and skipped units must be unaffected
+# launches of seven or eight drafts per unit reserve LDS so that one block
+# runs per CU; ragged and skipped units must be unaffected in a batch of
+# several rounds of blocks
 # --------------------------------------------------------------------------
 def test_capped_launch_ragged_spec(dev):
     """1,152 units (> 4 per CU on 256 CUs): ragged lengths 0..8 and every
