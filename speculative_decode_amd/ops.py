@@ -222,11 +222,22 @@ def make_layer(q, k, v, z, a, b, A_log, dt_bias, norm_weight, out, *, scale=None
         float(K ** -0.5 if scale is None else scale), float(norm_eps))
 
 
-def make_pool(state: torch.Tensor) -> GdnStatePool:
+def make_pool(state: torch.Tensor, layer: Optional[GdnLayer] = None,
+              device=None) -> GdnStatePool:
+    """Describe a state pool.  With ``layer``, its [HV, V, K] must be the
+    layer's: the kernels address tile (slot, h) as slot * HV + h with the
+    layer's HV, so a pool with fewer heads would be written past its end."""
     if state.dtype not in _STATE_DTYPE:
         raise ValueError("state pool must be float32, float16, bfloat16 or float8_e4m3fn")
     if state.dim() != 4 or not state.is_contiguous():
         raise ValueError("state pool must be a contiguous [num_slots, HV, V, K] tensor")
+    if layer is not None:
+        want = (layer.num_v_heads, layer.head_v_dim, layer.head_k_dim)
+        if tuple(state.shape[1:]) != want:
+            raise ValueError(f"state pool is [num_slots, {', '.join(map(str, state.shape[1:]))}]"
+                             f", the layer needs [num_slots, {', '.join(map(str, want))}]")
+    if device is not None and state.device != device:
+        raise ValueError(f"state pool is on {state.device}, the layer on {device}")
     return GdnStatePool(state.data_ptr(), _STATE_DTYPE[state.dtype], 0, state.shape[0])
 
 
@@ -263,7 +274,7 @@ def spec_decode_update(q, k, v, z, a, b, A_log, dt_bias, norm_weight, state,
     dev = q.device
     layer = make_layer(q, k, v, z, a, b, A_log, dt_bias, norm_weight, out,
                        scale=scale, norm_eps=norm_eps)
-    pool = make_pool(state)
+    pool = make_pool(state, layer, dev)
     cu = _meta(cu_seqlens, "cu_seqlens", dev)
     si = _meta(spec_state_indices, "spec_state_indices", dev)
     na = _meta(num_accepted_tokens, "num_accepted_tokens", dev)
@@ -289,7 +300,7 @@ def decode_update(q, k, v, z, a, b, A_log, dt_bias, norm_weight, state, state_in
     dev = q.device
     layer = make_layer(q, k, v, z, a, b, A_log, dt_bias, norm_weight, out,
                        scale=scale, norm_eps=norm_eps)
-    pool = make_pool(state)
+    pool = make_pool(state, layer, dev)
     si = _meta(state_indices, "state_indices", dev)
     ti = _meta(token_indx, "token_indx", dev)
     _check(lib.gdn_decode_update(ctypes.byref(layer), ctypes.byref(pool), _ptr(si),
@@ -309,7 +320,7 @@ def mixed_decode_update(q, k, v, z, a, b, A_log, dt_bias, norm_weight, state, cu
     dev = q.device
     layer = make_layer(q, k, v, z, a, b, A_log, dt_bias, norm_weight, out,
                        scale=scale, norm_eps=norm_eps)
-    pool = make_pool(state)
+    pool = make_pool(state, layer, dev)
     cu = _meta(cu_seqlens, "cu_seqlens", dev)
     si = _meta(spec_state_indices, "spec_state_indices", dev)
     na = _meta(num_accepted_tokens, "num_accepted_tokens", dev)
@@ -377,7 +388,7 @@ def prefill_update(q, k, v, z, a, b, A_log, dt_bias, norm_weight, state, cu_seql
     dev = q.device
     layer = make_layer(q, k, v, z, a, b, A_log, dt_bias, norm_weight, out,
                        scale=scale, norm_eps=norm_eps)
-    pool = make_pool(state)
+    pool = make_pool(state, layer, dev)
     cu = _meta(cu_seqlens, "cu_seqlens", dev)
     si = _meta(state_indices, "state_indices", dev)
     hi = _meta(has_initial_state, "has_initial_state", dev)
@@ -490,12 +501,19 @@ def make_conv_layer(x, weight, bias, out, *, activation="silu") -> GdnConvLayer:
         _DTYPE[x.dtype], _DTYPE[out.dtype], C, weight.shape[1], CONV_ACT[activation], 0, n_tok)
 
 
-def make_conv_cache(cache: torch.Tensor) -> GdnConvCache:
+def make_conv_cache(cache: torch.Tensor, layer: Optional[GdnConvLayer] = None,
+                    device=None) -> GdnConvCache:
     """A [num_lines, state_len, C] buffer with any strides (a channel-major
-    buffer is passed as ``buf.transpose(1, 2)``)."""
+    buffer is passed as ``buf.transpose(1, 2)``).  With ``layer``, C must be
+    the layer's channel count: the kernels index every channel of a line."""
     if cache.dim() != 3 or cache.dtype not in _DTYPE:
         raise ValueError("conv cache must be a float32/float16/bfloat16 "
                          "[num_lines, state_len, channels] tensor")
+    if layer is not None and cache.shape[2] != layer.channels:
+        raise ValueError(f"conv cache has {cache.shape[2]} channels, the layer "
+                         f"{layer.channels}")
+    if device is not None and cache.device != device:
+        raise ValueError(f"conv cache is on {cache.device}, x on {device}")
     return GdnConvCache(cache.data_ptr(), _DTYPE[cache.dtype], cache.shape[1], cache.shape[0],
                         cache.stride(0), cache.stride(1), cache.stride(2))
 
@@ -514,7 +532,7 @@ def conv_spec_update(x, weight, bias, cache, cu_seqlens, conv_indices, num_accep
         out = torch.zeros_like(x)
     dev = x.device
     layer = make_conv_layer(x, _conv_weight(weight), bias, out, activation=activation)
-    cc = make_conv_cache(cache)
+    cc = make_conv_cache(cache, layer, dev)
     cu = _meta(cu_seqlens, "cu_seqlens", dev)
     li = _meta(conv_indices, "conv_indices", dev)
     na = _meta(num_accepted_tokens, "num_accepted_tokens", dev)
@@ -536,7 +554,7 @@ def conv_decode_update(x, weight, bias, cache, conv_indices, *, token_indx=None,
         out = torch.zeros_like(x)
     dev = x.device
     layer = make_conv_layer(x, _conv_weight(weight), bias, out, activation=activation)
-    cc = make_conv_cache(cache)
+    cc = make_conv_cache(cache, layer, dev)
     li = _meta(conv_indices, "conv_indices", dev)
     ti = _meta(token_indx, "token_indx", dev)
     _check(lib.gdn_conv_decode_update(ctypes.byref(layer), ctypes.byref(cc), _ptr(li),

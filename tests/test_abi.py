@@ -147,6 +147,33 @@ def test_binding_checks_shapes_on_host():
         ops.make_pool(torch.zeros(2, 2, 128, 128).transpose(2, 3))
 
 
+def test_binding_rejects_a_pool_that_does_not_match_the_layer(lib):
+    """The kernels address tile (slot, h) as slot * HV + h with the layer's
+    HV, so every entry point checks the pool's [HV, V, K] against the layer
+    on the host, before anything is enqueued (CPU tensors: no device call)."""
+    n, HK, HV = 4, 1, 2
+    q = torch.zeros(n, HK, 128)
+    v = torch.zeros(n, HV, 128)
+    ab = torch.zeros(n, HV)
+    layer_args = (q, q, v, v, ab, ab, torch.zeros(HV), torch.zeros(HV), torch.ones(128))
+    cu = torch.tensor([0, 4], dtype=torch.int32)
+    si = torch.arange(4, dtype=torch.int32).reshape(1, 4)
+    na = torch.ones(1, dtype=torch.int32)
+    idx = torch.arange(n, dtype=torch.int32)
+    for bad in (torch.zeros(8, 1, 128, 128), torch.zeros(8, 4, 128, 128),
+                torch.zeros(8, HV, 64, 128), torch.zeros(8, HV, 128, 64)):
+        with pytest.raises(ValueError, match="the layer needs"):
+            ops.spec_decode_update(*layer_args, bad, cu, si, na)
+        with pytest.raises(ValueError, match="the layer needs"):
+            ops.decode_update(*layer_args, bad, idx)
+        with pytest.raises(ValueError, match="the layer needs"):
+            ops.mixed_decode_update(*layer_args, bad, cu, si, na, idx)
+        with pytest.raises(ValueError, match="the layer needs"):
+            ops.prefill_update(*layer_args, bad, cu, idx[:1])
+    layer = ops.make_layer(*layer_args, torch.zeros(n, HV, 128))
+    assert ops.make_pool(torch.zeros(8, HV, 128, 128), layer).num_slots == 8
+
+
 # -- metadata contract (host validator) ------------------------------------------
 def _validate(batch, num_slots=None, **over):
     args = dict(cu_seqlens=batch.cu_seqlens, spec_state_indices=batch.spec_state_indices,

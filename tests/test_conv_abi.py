@@ -108,6 +108,18 @@ def test_binding_checks_shapes_on_host():
         ops.make_conv_layer(x, torch.zeros(16, 4), None, torch.zeros(4, 16), activation="relu")
     with pytest.raises(ValueError):
         ops.make_conv_cache(torch.zeros(2, 3, 4, 5))
+    # the cache's channel count must be the layer's: every entry point checks
+    # it on the host before anything is enqueued
+    w = torch.zeros(16, 4)
+    cu = torch.tensor([0, 4], dtype=torch.int32)
+    one = torch.zeros(1, dtype=torch.int32)
+    for bad in (torch.zeros(2, 6, 8), torch.zeros(2, 6, 32)):
+        with pytest.raises(ValueError, match="channels"):
+            ops.conv_spec_update(x, w, None, bad, cu, one, one)
+        with pytest.raises(ValueError, match="channels"):
+            ops.conv_decode_update(x, w, None, bad, torch.zeros(4, dtype=torch.int32))
+    layer = ops.make_conv_layer(x, w, None, torch.zeros(4, 16))
+    assert ops.make_conv_cache(torch.zeros(2, 6, 16), layer).num_lines == 2
     # torch's depthwise conv1d weight [C, 1, W] is accepted as is
     L = ops.make_conv_layer(x, torch.zeros(16, 1, 4)[:, 0, :], None, torch.zeros(4, 16))
     assert L.width == 4 and L.channels == 16
