@@ -192,6 +192,13 @@ def _meta(t: Optional[torch.Tensor], name: str, device) -> Optional[torch.Tensor
     return t
 
 
+def _check_gather(tix: Optional[torch.Tensor], slots: torch.Tensor, tname: str, sname: str):
+    """Entry i of a single-token launch reads tix[i]: the gather index needs
+    an entry for every slot entry."""
+    if tix is not None and tix.numel() < slots.numel():
+        raise ValueError(f"{tname} has {tix.numel()} entries, {sname} {slots.numel()}")
+
+
 def make_layer(q, k, v, z, a, b, A_log, dt_bias, norm_weight, out, *, scale=None,
                norm_eps=1e-5) -> GdnLayer:
     """Describe one layer's device tensors as a gdn_layer (no data is touched)."""
@@ -303,6 +310,7 @@ def decode_update(q, k, v, z, a, b, A_log, dt_bias, norm_weight, state, state_in
     pool = make_pool(state, layer, dev)
     si = _meta(state_indices, "state_indices", dev)
     ti = _meta(token_indx, "token_indx", dev)
+    _check_gather(ti, si, "token_indx", "state_indices")
     _check(lib.gdn_decode_update(ctypes.byref(layer), ctypes.byref(pool), _ptr(si),
                                  si.shape[0], _ptr(ti), _stream(dev)))
     return out
@@ -327,6 +335,7 @@ def mixed_decode_update(q, k, v, z, a, b, A_log, dt_bias, norm_weight, state, cu
     st = _meta(spec_token_indx, "spec_token_indx", dev)
     ns = _meta(state_indices, "state_indices", dev)
     nst = _meta(non_spec_token_indx, "non_spec_token_indx", dev)
+    _check_gather(nst, ns, "non_spec_token_indx", "state_indices")
     if si.dim() != 2:
         raise ValueError("spec_state_indices must be [num_seqs, spec_stride]")
     B = cu.shape[0] - 1
@@ -557,6 +566,7 @@ def conv_decode_update(x, weight, bias, cache, conv_indices, *, token_indx=None,
     cc = make_conv_cache(cache, layer, dev)
     li = _meta(conv_indices, "conv_indices", dev)
     ti = _meta(token_indx, "token_indx", dev)
+    _check_gather(ti, li, "token_indx", "conv_indices")
     _check(lib.gdn_conv_decode_update(ctypes.byref(layer), ctypes.byref(cc), _ptr(li),
                                       li.shape[0], _ptr(ti), _stream(dev)))
     return out

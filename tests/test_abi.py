@@ -172,6 +172,13 @@ def test_binding_rejects_a_pool_that_does_not_match_the_layer(lib):
             ops.prefill_update(*layer_args, bad, cu, idx[:1])
     layer = ops.make_layer(*layer_args, torch.zeros(n, HV, 128))
     assert ops.make_pool(torch.zeros(8, HV, 128, 128), layer).num_slots == 8
+    # a single-token gather index needs an entry per slot entry
+    pool = torch.zeros(8, HV, 128, 128)
+    with pytest.raises(ValueError, match="token_indx has 3 entries"):
+        ops.decode_update(*layer_args, pool, idx, token_indx=idx[:3])
+    with pytest.raises(ValueError, match="non_spec_token_indx has 2 entries"):
+        ops.mixed_decode_update(*layer_args, pool, cu, si, na, idx[:3],
+                                non_spec_token_indx=idx[:2])
 
 
 # -- metadata contract (host validator) ------------------------------------------

@@ -120,6 +120,10 @@ def test_binding_checks_shapes_on_host():
             ops.conv_decode_update(x, w, None, bad, torch.zeros(4, dtype=torch.int32))
     layer = ops.make_conv_layer(x, w, None, torch.zeros(4, 16))
     assert ops.make_conv_cache(torch.zeros(2, 6, 16), layer).num_lines == 2
+    with pytest.raises(ValueError, match="token_indx has 2 entries"):
+        ops.conv_decode_update(x, w, None, torch.zeros(2, 6, 16),
+                               torch.zeros(4, dtype=torch.int32),
+                               token_indx=torch.zeros(2, dtype=torch.int32))
     # torch's depthwise conv1d weight [C, 1, W] is accepted as is
     L = ops.make_conv_layer(x, torch.zeros(16, 1, 4)[:, 0, :], None, torch.zeros(4, 16))
     assert L.width == 4 and L.channels == 16
