@@ -41,7 +41,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, AMD's published figure
-PEAK_FP32_TFLOPS = 157.3       # MI355X FP32 vector, AMD's published figure
+PEAK_FP32_TFLOPS = 157.3       # MI355X dense FP32 (matrix cores; also packed vector), AMD's published figure
 DEFAULT_WORKLOAD = {"gdn": "mtp_b128_bf16", "conv": "conv_mtp_b128",
                     "prefill": "prefill_b16_l2048"}
 DEFAULT_LAYERS = {"gdn": 4, "conv": 32, "prefill": 2}
@@ -479,7 +479,7 @@ def bench_prefill(args, dev):
                    "algorithmic_bytes_per_step": batch.algorithmic_bytes(),
                    "achieved_hbm_gbs": batch.algorithmic_bytes() / avg_s / 1e9,
                    "layers_cycled": len(layers)},
-        "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_TFLOPS,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP32_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_TFLOPS,
                      "traffic": recorded_traffic(args.workload, "prefill"), **tf},
         "cpu_baseline": prefill_cpu_baseline(batch) if args.cpu_seqs > 0 else None,

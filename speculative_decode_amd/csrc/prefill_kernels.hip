@@ -8,28 +8,31 @@
 // throughout, the state rounded to its storage dtype once per chunk, when the
 // chunk's state is written back.  gdn_spec.h spells out the formula.
 //
-// How it is computed here:
-//   * One 512-thread workgroup per (sequence, value head), the 128 x 128
-//     state in registers with the decode kernel's lane layout (each 8-lane
-//     group owns a row at a time, each lane 16 elements), spread over eight
-//     waves -- 2 rows per lane -- so that a SIMD has more waves to hide the
-//     latency of each token's LDS reads and reductions.  The state is
-//     read once, rounded in registers at every chunk end, and written once:
-//     intermediate chunk write-backs go to the same slot and are overwritten,
-//     so only the rounding is kept, not the stores.
-//   * Tokens are taken 8 at a time.  The normalised q/k, v, z, the gates and
-//     k^.q^ of a step are staged in LDS (double-buffered), and the next
-//     step's activation loads are issued before this step's token loop, so
-//     their latency hides behind the recurrence.
-//   * Why not the chunkwise (WY / UT-transform) form: it trades the serial
-//     recurrence for dense C x C, C x K and K x V products per chunk -- about
-//     1.6x the arithmetic at C = 64, plus a triangular solve -- to run them on
-//     matrix cores.  The pages fix FP32 arithmetic.  The FP32 matrix rate of
-//     MI355X is twice the non-packed vector rate this kernel issues at, so
-//     even small products running at the matrix peak would gain at most
-//     about 1.25x; BF16 matrix operands would give up the FP32 arithmetic.
-//   * Prefill is compute-bound (about 130 flop per byte of HBM traffic): the
-//     roofline is the FP32 vector ALU.
+// How it is computed here -- two kernels, one (sequence, value head) unit per
+// workgroup, chosen by chunk size:
+//   * chunk_size >= 16: the chunkwise form on the FP32 matrix cores
+//     (gdn_prefill_mma_kernel).  Tokens go 16 at a time (never across a chunk
+//     end).  Within such a sub-chunk the token recurrence unrolls into dense
+//     products, S0 [k^ | q^] and the state update S <- e^{G} S + D' K^T,
+//     which run on v_mfma_f32_32x32x2f32, plus a 16 x 16 triangular solve
+//     per value row on the vector ALU.  The decays are carried as sums of
+//     log(alpha), so no product of decays under- or overflows.  The state
+//     stays transposed in the matrix-core accumulator layout, which is also
+//     the operand layout S0 needs for S0 [k^ | q^]: it never moves between
+//     the two products.  About 6 K V flop per token and head against the
+//     recurrence's 7, at twice the rate of non-packed FP32 vector issue.
+//   * chunk_size < 16: the token recurrence itself (gdn_prefill_kernel): the
+//     128 x 128 state in registers with the decode kernel's lane layout
+//     (each 8-lane group owns a row at a time, each lane 16 elements), over
+//     eight waves -- 2 rows per lane -- so that a SIMD has more waves to hide
+//     the latency of each token's LDS reads and reductions.  Tokens are
+//     taken 8 at a time; their normalised q/k, v, z, gates and k^.q^ are
+//     staged in LDS (double-buffered), the next step's loads issued before
+//     this step's token loop.
+//   * Both read the state once, round it in registers at every chunk end,
+//     and write it once: intermediate chunk write-backs go to the same slot
+//     and are overwritten, so only the rounding is kept, not the stores.
+//   * Prefill is compute-bound (about 130 flop per byte of HBM traffic).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -304,11 +307,351 @@ gdn_prefill_kernel(const PParams p)
     }
 }
 
+// ---- the chunkwise form on the FP32 matrix cores ---------------------------
+// Within a sub-chunk of up to MC tokens starting from state S0, with
+// G_t = sum_{j<=t} log(alpha_j) (log decays, so no product under- or
+// overflows):
+//   S_t      = e^{G_t} S0 + sum_{i<=t} e^{G_t - G_i} d_i k^_i^T
+//   d_t      = beta_t (v_t - e^{G_t} S0 k^_t - sum_{i<t} e^{G_t-G_i} (k^_i.k^_t) d_i)
+//   o_t      = e^{G_t} S0 q^_t + sum_{i<=t} e^{G_t-G_i} (k^_i.q^_t) d_i
+// -- the token recurrence unrolled, the same values up to rounding order.
+// The products S0 [k^ | q^] (V x K by K x 2MC) and the update
+// S <- e^{G_end} S + D' K^T (D'_i = e^{G_end - G_i} d_i) run on
+// v_mfma_f32_32x32x2f32; the MC x MC triangular solve for d runs on the
+// vector ALU, one value row per lane.
+//
+// Layout: wave w owns value rows v = 32w..32w+31.  The state is kept
+// transposed in the matrix-core accumulator layout: element r of tile kb in
+// lane l is S[32w + l%32][32kb + 8(r/4) + 4(l/32) + r%4].  That is also the
+// A-operand layout of S0 for S0 X (lane l supplies row l%32, and the two
+// lane halves the two k of a step), so the state never moves between the
+// two products.
+constexpr int MC = 16;            // tokens per sub-chunk
+constexpr int MT = 256;           // threads per block: 4 waves
+constexpr int XP = D + 4;         // padded row stride of the staged k^ / q^ rows
+constexpr int PP = 33;            // padded row stride of the 32 x 32 transposes
+constexpr int MTW = MC / (MT / 64);   // tokens staged per wave
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+struct MStage {
+    float x[2 * MC][XP];          // rows t: k^_t, rows MC + t: q^_t (zero past the sub-chunk)
+    float v[MC][D];
+    float p[4][2 * MC][PP];       // per wave: S0 [k^|q^], [token column][value row]
+    union {
+        float gp[4][2 * MC][PP];  // per wave: partial Gram matrix [k^|q^]^T [k^|q^]
+        float o[MC][D];           // the sub-chunk's read-outs
+    } u;
+    float akk[MC][MC];            // [t][i]: e^{G_t-G_i} k^_i.k^_t for i < t, else 0
+    float bkq[MC][MC];            // [t][i]: e^{G_t-G_i} k^_i.q^_t for i <= t, else 0
+    float gam[MC];                // e^{G_t}
+    float wend[MC];               // e^{G_end - G_t}
+    float g[MC];                  // log alpha_t (0 past the sub-chunk)
+    float beta[MC];               // (0 past the sub-chunk)
+    int64_t row[MC];
+};
+
+template <int ACT>
+struct MRaw {
+    typename Pair<ACT>::raw q[MTW], k[MTW], v[MTW], z[MTW];
+    uint32_t a[MTW], b[MTW];
+    int64_t row[MTW];
+};
+
+// Tokens of one sub-chunk for this wave: t = wave + 4 i.
+template <int ACT>
+__device__ __forceinline__ void issue_sub(const PParams& p, int64_t c0, int L, int pos,
+                                          int wave, int lane, int h, int kh, MRaw<ACT>& r)
+{
+#pragma unroll
+    for (int i = 0; i < MTW; ++i) {
+        const int t = pos + wave + 4 * i;
+        const int tt = t < L ? t : L - 1;
+        const int64_t row = p.tix ? static_cast<int64_t>(p.tix[c0 + tt]) : c0 + tt;
+        r.row[i] = row;
+        r.q[i] = load_pair_raw<ACT>(p.q, row * p.q_st + kh * p.q_sh + 2 * lane);
+        r.k[i] = load_pair_raw<ACT>(p.k, row * p.k_st + kh * p.k_sh + 2 * lane);
+        r.v[i] = load_pair_raw<ACT>(p.v, row * p.v_st + h * p.v_sh + 2 * lane);
+        r.z[i] = load_pair_raw<ACT>(p.z, row * p.z_st + h * p.z_sh + 2 * lane);
+        r.a[i] = load_one_raw<ACT>(p.a, row * p.a_st + h);
+        r.b[i] = load_one_raw<ACT>(p.b, row * p.b_st + h);
+    }
+}
+
+// Tokens in the sub-chunk at pos: up to MC, never across a chunk end.
+__device__ __forceinline__ int sub_len(int pos, int L, int chunk)
+{
+    int n = L - pos < MC ? L - pos : MC;
+    const int to_end = chunk - pos % chunk;
+    return n < to_end ? n : to_end;
+}
+
+// Four consecutive state elements (k contiguous) to / from fp32.
+template <int ST>
+__device__ __forceinline__ void load4_state(const char* base, size_t e, float* f)
+{
+    if constexpr (ST == GDN_F32) {
+        const uint4 w = *reinterpret_cast<const uint4*>(base + e * 4);
+        f[0] = __uint_as_float(w.x); f[1] = __uint_as_float(w.y);
+        f[2] = __uint_as_float(w.z); f[3] = __uint_as_float(w.w);
+    } else if constexpr (ST == GDN_F8E4M3) {
+        unpack4_f8(*reinterpret_cast<const uint32_t*>(base + e), f[0], f[1], f[2], f[3]);
+    } else {
+        const uint2 w = *reinterpret_cast<const uint2*>(base + e * 2);
+        const float2 lo = unpack_pair<ST>(w.x), hi = unpack_pair<ST>(w.y);
+        f[0] = lo.x; f[1] = lo.y; f[2] = hi.x; f[3] = hi.y;
+    }
+}
+
+template <int ST>
+__device__ __forceinline__ void store4_state(char* base, size_t e, const float* f)
+{
+    if constexpr (ST == GDN_F32) {
+        *reinterpret_cast<uint4*>(base + e * 4) =
+            make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                       __float_as_uint(f[3]));
+    } else if constexpr (ST == GDN_F8E4M3) {
+        *reinterpret_cast<uint32_t*>(base + e) = pack4_f8(f[0], f[1], f[2], f[3]);
+    } else {
+        *reinterpret_cast<uint2*>(base + e * 2) =
+            make_uint2(pack2<ST>(f[0], f[1]), pack2<ST>(f[2], f[3]));
+    }
+}
+
+template <int ACT, int ST, int OUT>
+__global__ void __launch_bounds__(MT) __attribute__((amdgpu_waves_per_eu(2)))
+gdn_prefill_mma_kernel(const PParams p)
+{
+    constexpr int ESZ = ST == GDN_F32 ? 4 : (ST == GDN_F8E4M3 ? 1 : 2);
+    __shared__ __attribute__((aligned(16))) MStage sm;
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int lc = lane & 31;
+    const int lh = lane >> 5;
+
+    const uint32_t nblk = gridDim.x;
+    const uint32_t xcd = blockIdx.x % NXCD;
+    const uint32_t per = nblk / NXCD, rem = nblk % NXCD;
+    const uint32_t unit = xcd * per + (xcd < rem ? xcd : rem) + blockIdx.x / NXCD;
+    const uint32_t seq32 = unit / static_cast<uint32_t>(p.HV);
+    const int64_t seq = seq32;
+    const int h = static_cast<int>(unit - seq32 * static_cast<uint32_t>(p.HV));
+    const int kh = static_cast<int>(static_cast<uint32_t>(h) / static_cast<uint32_t>(p.group));
+
+    const int64_t c0 = p.cu[seq];
+    const int L = static_cast<int>(p.cu[seq + 1] - c0);
+    const int64_t slot = p.state_idx[seq];
+    if (L <= 0 || slot < 0)
+        return;
+    bool bad = slot >= p.num_slots || c0 < 0;
+    for (int t = tid; t < L && !bad; t += MT) {
+        const int64_t row = p.tix ? static_cast<int64_t>(p.tix[c0 + t]) : c0 + t;
+        bad = row < 0 || row >= p.n_tok;
+    }
+    if (__syncthreads_or(bad))
+        return;
+    const bool init = p.has_init ? p.has_init[seq] != 0 : true;
+
+    // ---- the state, transposed into the accumulator layout ----
+    const size_t tile = static_cast<size_t>(D) * D;
+    char* sbase = static_cast<char*>(p.pool) + (static_cast<size_t>(slot) * p.HV + h) * tile * ESZ;
+    const int vrow = 32 * wave + lc;
+    f32x16 S[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            float f[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (init)
+                load4_state<ST>(sbase, static_cast<size_t>(vrow) * D + 32 * kb + 8 * q + 4 * lh, f);
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                S[kb][4 * q + m] = f[m];
+        }
+
+    const float A = -expf(p.A_log[h]);
+    const float dtb = p.dt_bias[h];
+    const float2 wn = *reinterpret_cast<const float2*>(p.norm_weight + 2 * lane);
+
+    for (int pos = 0; pos < L;) {
+        const int n = sub_len(pos, L, p.chunk);
+        const int next = pos + n;
+        MRaw<ACT> raw;
+        issue_sub<ACT>(p, c0, L, pos, wave, lane, h, kh, raw);
+
+        // ---- stage: normalised k and q, v, gates; z stays in registers ----
+        float2 zc[MTW];
+#pragma unroll
+        for (int i = 0; i < MTW; ++i) {
+            const int t = wave + 4 * i;
+            const bool live = t < n;
+            const float2 qv = unpack_pair<ACT>(raw.q[i]);
+            const float2 kv = unpack_pair<ACT>(raw.k[i]);
+            const float nq = sum64(qv.x * qv.x + qv.y * qv.y);
+            const float nk = sum64(kv.x * kv.x + kv.y * kv.y);
+            const float rk = live ? frsqrt(nk + 1e-6f) : 0.0f;
+            const float rq = live ? p.scale * frsqrt(nq + 1e-6f) : 0.0f;
+            const float2 vv = unpack_pair<ACT>(raw.v[i]);
+            zc[i] = unpack_pair<ACT>(raw.z[i]);
+            *reinterpret_cast<float2*>(&sm.x[t][2 * lane]) =
+                live ? make_float2(kv.x * rk, kv.y * rk) : make_float2(0.0f, 0.0f);
+            *reinterpret_cast<float2*>(&sm.x[MC + t][2 * lane]) =
+                live ? make_float2(qv.x * rq, qv.y * rq) : make_float2(0.0f, 0.0f);
+            *reinterpret_cast<float2*>(&sm.v[t][2 * lane]) =
+                live ? vv : make_float2(0.0f, 0.0f);
+            if (lane == 0) {
+                sm.row[t] = raw.row[i];
+                const float x = unpack_one<ACT>(raw.a[i]) + dtb;
+                sm.g[t] = live ? A * softplus_fast(x) : 0.0f;
+                sm.beta[t] = live ? sigmoid_fast(unpack_one<ACT>(raw.b[i])) : 0.0f;
+            }
+        }
+        __syncthreads();
+
+        // ---- S0 [k^ | q^] and this wave's share of the Gram matrix ----
+        f32x16 P = {};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 xb =
+                    *reinterpret_cast<const float4*>(&sm.x[lc][32 * kb + 8 * q + 4 * lh]);
+                P = __builtin_amdgcn_mfma_f32_32x32x2f32(S[kb][4 * q + 0], xb.x, P, 0, 0, 0);
+                P = __builtin_amdgcn_mfma_f32_32x32x2f32(S[kb][4 * q + 1], xb.y, P, 0, 0, 0);
+                P = __builtin_amdgcn_mfma_f32_32x32x2f32(S[kb][4 * q + 2], xb.z, P, 0, 0, 0);
+                P = __builtin_amdgcn_mfma_f32_32x32x2f32(S[kb][4 * q + 3], xb.w, P, 0, 0, 0);
+            }
+        f32x16 Gm = {};
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+            const float xv = sm.x[lc][32 * wave + 2 * s + lh];
+            Gm = __builtin_amdgcn_mfma_f32_32x32x2f32(xv, xv, Gm, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int i = 8 * (r / 4) + 4 * lh + r % 4;
+            sm.p[wave][lc][i] = P[r];          // [token column][value row]
+            sm.u.gp[wave][i][lc] = Gm[r];      // [column i][column j]
+        }
+        __syncthreads();
+
+        // ---- decay-weighted Gram coefficients (one (i, t) pair per thread) ----
+        {
+            const int i = tid / MC, t = tid % MC;
+            float Gi = 0.0f, Gt = 0.0f, Ge = 0.0f;
+#pragma unroll
+            for (int j = 0; j < MC; ++j) {
+                const float gj = sm.g[j];
+                Gi += j <= i ? gj : 0.0f;
+                Gt += j <= t ? gj : 0.0f;
+                Ge += gj;
+            }
+            const float kk = (sm.u.gp[0][i][t] + sm.u.gp[1][i][t]) +
+                             (sm.u.gp[2][i][t] + sm.u.gp[3][i][t]);
+            const float kq = (sm.u.gp[0][i][MC + t] + sm.u.gp[1][i][MC + t]) +
+                             (sm.u.gp[2][i][MC + t] + sm.u.gp[3][i][MC + t]);
+            const float e = i <= t ? fexp(Gt - Gi) : 0.0f;
+            sm.akk[t][i] = i < t ? e * kk : 0.0f;
+            sm.bkq[t][i] = e * kq;
+            if (i == 0) {
+                sm.gam[t] = fexp(Gt);
+                sm.wend[t] = fexp(Ge - Gt);
+            }
+        }
+        __syncthreads();
+
+        // ---- the triangular solve for d, and the read-outs: value row
+        // 32 wave + lc per lane; the lane halves split the read-outs ----
+        float d[MC];
+#pragma unroll
+        for (int t = 0; t < MC; ++t) {
+            float acc = sm.gam[t] * sm.p[wave][t][lc];
+#pragma unroll
+            for (int i = 0; i < t; ++i)
+                acc = fmaf(sm.akk[t][i], d[i], acc);
+            d[t] = sm.beta[t] * (sm.v[t][vrow] - acc);
+        }
+#pragma unroll
+        for (int tt = 0; tt < MC / 2; ++tt) {
+            const int t = tt + (MC / 2) * lh;
+            float o = sm.gam[t] * sm.p[wave][MC + t][lc];
+#pragma unroll
+            for (int i = 0; i < MC; ++i)
+                o = fmaf(sm.bkq[t][i], d[i], o);
+            sm.u.o[t][vrow] = o;
+        }
+
+        // ---- S <- e^{G_end} S + D' K^T ----
+        const float ge = sm.gam[MC - 1];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                S[kb][r] *= ge;
+#pragma unroll
+        for (int s = 0; s < MC / 2; ++s) {
+            const float b = lh ? sm.wend[2 * s + 1] * d[2 * s + 1] : sm.wend[2 * s] * d[2 * s];
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+                S[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(sm.x[2 * s + lh][32 * kb + lc], b,
+                                                             S[kb], 0, 0, 0);
+        }
+        // chunk end: the state continues from its stored (rounded) value
+        if (next % p.chunk == 0 && next < L) {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; r += 2) {
+                    float x0 = S[kb][r], x1 = S[kb][r + 1];
+                    round_pair<ST>(x0, x1);
+                    S[kb][r] = x0;
+                    S[kb][r + 1] = x1;
+                }
+        }
+        __syncthreads();
+
+        // ---- gated RMSNorm over V per (token, head) ----
+#pragma unroll
+        for (int i = 0; i < MTW; ++i) {
+            const int t = wave + 4 * i;
+            if (t < n) {
+                const float2 o = *reinterpret_cast<const float2*>(&sm.u.o[t][2 * lane]);
+                const int64_t row = sm.row[t];
+                const float ms = sum64(o.x * o.x + o.y * o.y) * (1.0f / D);
+                const float rr = frsqrt(ms + p.norm_eps);
+                const float gx = zc[i].x * sigmoid_fast(zc[i].x);
+                const float gy = zc[i].y * sigmoid_fast(zc[i].y);
+                const float2 y = make_float2(o.x * rr * wn.x * gx, o.y * rr * wn.y * gy);
+                store_pair<OUT>(p.out, row * p.o_st + h * p.o_sh + 2 * lane, y);
+            }
+        }
+        __syncthreads();
+        pos = next;
+    }
+
+    // ---- the final state, rounded once, written once ----
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            float f[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                f[m] = S[kb][4 * q + m];
+            store4_state<ST>(sbase, static_cast<size_t>(vrow) * D + 32 * kb + 8 * q + 4 * lh, f);
+        }
+}
+
 template <int A, int S, int O>
 hipError_t launch_typed(const PParams& p, int64_t grid, hipStream_t stream)
 {
     PParams args = p;
     void* argv[] = {&args};
+    if (p.chunk >= MC)
+        return hipLaunchKernel(reinterpret_cast<const void*>(&gdn_prefill_mma_kernel<A, S, O>),
+                               dim3(static_cast<uint32_t>(grid)), dim3(MT), argv, 0, stream);
     return hipLaunchKernel(reinterpret_cast<const void*>(&gdn_prefill_kernel<A, S, O>),
                            dim3(static_cast<uint32_t>(grid)), dim3(NTHREADS), argv, 0, stream);
 }
