@@ -510,7 +510,10 @@ gdn_prefill_mma_kernel(const PParams p)
         }
         __syncthreads();
 
-        // ---- S0 [k^ | q^] and this wave's share of the Gram matrix ----
+        // ---- S0 [k^ | q^] and this wave's share of the Gram matrix.  The
+        // matrix phases run at raised wave priority, so that the other block
+        // on the SIMD fills the gaps with its vector work. ----
+        __builtin_amdgcn_s_setprio(2);
         f32x16 P = {};
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
@@ -529,6 +532,7 @@ gdn_prefill_mma_kernel(const PParams p)
             const float xv = sm.x[lc][32 * wave + 2 * s + lh];
             Gm = __builtin_amdgcn_mfma_f32_32x32x2f32(xv, xv, Gm, 0, 0, 0);
         }
+        __builtin_amdgcn_s_setprio(0);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int i = 8 * (r / 4) + 4 * lh + r % 4;
@@ -564,14 +568,20 @@ gdn_prefill_mma_kernel(const PParams p)
 
         // ---- the triangular solve for d, and the read-outs: value row
         // 32 wave + lc per lane; the lane halves split the read-outs ----
-        float d[MC];
+        // Right-looking: once d_i is known it is folded into every later
+        // accumulator, which keeps each sum in ascending i (the same bits as
+        // summing row by row) and leaves only one FMA per step on the chain
+        // from d_i to d_{i+1}.
+        float d[MC], acc[MC];
 #pragma unroll
-        for (int t = 0; t < MC; ++t) {
-            float acc = sm.gam[t] * sm.p[wave][t][lc];
+        for (int t = 0; t < MC; ++t)
+            acc[t] = sm.gam[t] * sm.p[wave][t][lc];
 #pragma unroll
-            for (int i = 0; i < t; ++i)
-                acc = fmaf(sm.akk[t][i], d[i], acc);
-            d[t] = sm.beta[t] * (sm.v[t][vrow] - acc);
+        for (int i = 0; i < MC; ++i) {
+            d[i] = sm.beta[i] * (sm.v[i][vrow] - acc[i]);
+#pragma unroll
+            for (int t = i + 1; t < MC; ++t)
+                acc[t] = fmaf(sm.akk[t][i], d[i], acc[t]);
         }
 #pragma unroll
         for (int tt = 0; tt < MC / 2; ++tt) {
@@ -585,6 +595,7 @@ gdn_prefill_mma_kernel(const PParams p)
 
         // ---- S <- e^{G_end} S + D' K^T ----
         const float ge = sm.gam[MC - 1];
+        __builtin_amdgcn_s_setprio(2);
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -598,6 +609,7 @@ gdn_prefill_mma_kernel(const PParams p)
                 S[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(sm.x[2 * s + lh][32 * kb + lc], b,
                                                              S[kb], 0, 0, 0);
         }
+        __builtin_amdgcn_s_setprio(0);
         // chunk end: the state continues from its stored (rounded) value
         if (next % p.chunk == 0 && next < L) {
 #pragma unroll
