@@ -206,7 +206,11 @@ gdn_status gdn_mixed_decode_update(const gdn_layer* layer, const gdn_state_pool*
  * call and after its last -- where the chunked kernels of the pages write
  * the state back -- and continues from the rounded value.  A call split at
  * a multiple of chunk_size therefore equals one call.  Slots distinct per
- * call (gdn_validate_prefill_indices_host checks it).
+ * call (gdn_validate_prefill_indices_host checks it).  Arithmetic is FP32.
+ * With chunk_size >= 16 the rows of a chunk are taken 16 at a time in the
+ * chunkwise form of the same recurrence (matrix products plus a small
+ * triangular solve), which differs from row-by-row evaluation only in
+ * rounding order; results are deterministic for a given chunk_size.
  */
 gdn_status gdn_prefill_update(const gdn_layer* layer, const gdn_state_pool* pool,
                               const int32_t* cu_seqlens, int32_t num_seqs,
