@@ -347,6 +347,7 @@ struct MStage {
     float gam[MC];                // e^{G_t}
     float wend[MC];               // e^{G_end - G_t}
     float g[MC];                  // log alpha_t (0 past the sub-chunk)
+    float G[MC];                  // running sums of g: G_t = g_0 + ... + g_t
     float beta[MC];               // (0 past the sub-chunk)
     int64_t row[MC];
 };
@@ -526,6 +527,16 @@ gdn_prefill_mma_kernel(const PParams p)
                 P = __builtin_amdgcn_mfma_f32_32x32x2f32(S[kb][4 * q + 2], xb.z, P, 0, 0, 0);
                 P = __builtin_amdgcn_mfma_f32_32x32x2f32(S[kb][4 * q + 3], xb.w, P, 0, 0, 0);
             }
+        // the running sums of the log decays, by one lane, while the
+        // products run; the barrier below publishes them
+        if (tid == 0) {
+            float run = 0.0f;
+#pragma unroll
+            for (int j = 0; j < MC; ++j) {
+                run += sm.g[j];
+                sm.G[j] = run;
+            }
+        }
         f32x16 Gm = {};
 #pragma unroll
         for (int s = 0; s < 16; ++s) {
@@ -544,14 +555,7 @@ gdn_prefill_mma_kernel(const PParams p)
         // ---- decay-weighted Gram coefficients (one (i, t) pair per thread) ----
         {
             const int i = tid / MC, t = tid % MC;
-            float Gi = 0.0f, Gt = 0.0f, Ge = 0.0f;
-#pragma unroll
-            for (int j = 0; j < MC; ++j) {
-                const float gj = sm.g[j];
-                Gi += j <= i ? gj : 0.0f;
-                Gt += j <= t ? gj : 0.0f;
-                Ge += gj;
-            }
+            const float Gi = sm.G[i], Gt = sm.G[t], Ge = sm.G[MC - 1];
             const float kk = (sm.u.gp[0][i][t] + sm.u.gp[1][i][t]) +
                              (sm.u.gp[2][i][t] + sm.u.gp[3][i][t]);
             const float kq = (sm.u.gp[0][i][MC + t] + sm.u.gp[1][i][MC + t]) +
