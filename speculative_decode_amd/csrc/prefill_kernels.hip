@@ -333,13 +333,15 @@ constexpr int PP = 33;            // padded row stride of the 32 x 32 transposes
 constexpr int MTW = MC / (MT / 64);   // tokens staged per wave
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+constexpr int GP = MC + 1;        // padded row stride of the Gram tiles
 
 struct MStage {
     float x[2 * MC][XP];          // rows t: k^_t, rows MC + t: q^_t (zero past the sub-chunk)
     float v[MC][D];
     float p[4][2 * MC][PP];       // per wave: S0 [k^|q^], [token column][value row]
     union {
-        float gp[4][2 * MC][PP];  // per wave: partial Gram matrix [k^|q^]^T [k^|q^]
+        float gp[2][2][MC][GP];   // [K half][k^ or q^ columns][i][j]: partial k^_i . (k^|q^)_j
         float o[MC][D];           // the sub-chunk's read-outs
     } u;
     float akk[MC][MC];            // [t][i]: e^{G_t-G_i} k^_i.k^_t for i < t, else 0
@@ -537,29 +539,33 @@ gdn_prefill_mma_kernel(const PParams p)
                 sm.G[j] = run;
             }
         }
-        f32x16 Gm = {};
+        // k^_i . k^_t and k^_i . q^_t over this wave's half of K, on the
+        // 16 x 16 x 4 form: only the k^ rows of the Gram matrix are needed
+        const int gcol = wave & 1, gk = 64 * (wave >> 1), l16 = lane & 15, lq = lane >> 4;
+        f32x4 Gm = {};
 #pragma unroll
         for (int s = 0; s < 16; ++s) {
-            const float xv = sm.x[lc][32 * wave + 2 * s + lh];
-            Gm = __builtin_amdgcn_mfma_f32_32x32x2f32(xv, xv, Gm, 0, 0, 0);
+            const int k = gk + 4 * s + lq;
+            Gm = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.x[l16][k], sm.x[MC * gcol + l16][k], Gm,
+                                                      0, 0, 0);
         }
         __builtin_amdgcn_s_setprio(0);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int i = 8 * (r / 4) + 4 * lh + r % 4;
             sm.p[wave][lc][i] = P[r];          // [token column][value row]
-            sm.u.gp[wave][i][lc] = Gm[r];      // [column i][column j]
         }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            sm.u.gp[wave >> 1][gcol][4 * lq + r][l16] = Gm[r];
         __syncthreads();
 
         // ---- decay-weighted Gram coefficients (one (i, t) pair per thread) ----
         {
             const int i = tid / MC, t = tid % MC;
             const float Gi = sm.G[i], Gt = sm.G[t], Ge = sm.G[MC - 1];
-            const float kk = (sm.u.gp[0][i][t] + sm.u.gp[1][i][t]) +
-                             (sm.u.gp[2][i][t] + sm.u.gp[3][i][t]);
-            const float kq = (sm.u.gp[0][i][MC + t] + sm.u.gp[1][i][MC + t]) +
-                             (sm.u.gp[2][i][MC + t] + sm.u.gp[3][i][MC + t]);
+            const float kk = sm.u.gp[0][0][i][t] + sm.u.gp[1][0][i][t];
+            const float kq = sm.u.gp[0][1][i][t] + sm.u.gp[1][1][i][t];
             const float e = i <= t ? fexp(Gt - Gi) : 0.0f;
             sm.akk[t][i] = i < t ? e * kk : 0.0f;
             sm.bkq[t][i] = e * kq;
