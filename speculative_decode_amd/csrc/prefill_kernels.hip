@@ -340,10 +340,8 @@ struct MStage {
     float x[2 * MC][XP];          // rows t: k^_t, rows MC + t: q^_t (zero past the sub-chunk)
     float v[MC][D];
     float p[4][2 * MC][PP];       // per wave: S0 [k^|q^], [token column][value row]
-    union {
-        float gp[2][2][MC][GP];   // [K half][k^ or q^ columns][i][j]: partial k^_i . (k^|q^)_j
-        float o[MC][D];           // the sub-chunk's read-outs
-    } u;
+    float gp[2][2][MC][GP];       // [K half][k^ or q^ columns][i][j]: partial k^_i . (k^|q^)_j
+    float o[MC][D];               // the read-outs, until the next sub-chunk's products ran
     float akk[MC][MC];            // [t][i]: e^{G_t-G_i} k^_i.k^_t for i < t, else 0
     float bkq[MC][MC];            // [t][i]: e^{G_t-G_i} k^_i.q^_t for i <= t, else 0
     float gam[MC];                // e^{G_t}
@@ -351,7 +349,6 @@ struct MStage {
     float g[MC];                  // log alpha_t (0 past the sub-chunk)
     float G[MC];                  // running sums of g: G_t = g_0 + ... + g_t
     float beta[MC];               // (0 past the sub-chunk)
-    int64_t row[MC];
 };
 
 template <int ACT>
@@ -421,6 +418,28 @@ __device__ __forceinline__ void store4_state(char* base, size_t e, const float* 
     }
 }
 
+// Gated RMSNorm over V per (token, head) for this wave's tokens t = wave + 4 i
+// of a sub-chunk of n tokens, from its read-outs o.
+template <int OUT>
+__device__ __forceinline__ void epilogue(const PParams& p, const float (&o)[MC][D],
+                                         const float2 (&z)[MTW], const int64_t (&rows)[MTW],
+                                         int n, int wave, int lane, int h, float2 wn)
+{
+#pragma unroll
+    for (int i = 0; i < MTW; ++i) {
+        const int t = wave + 4 * i;
+        if (t < n) {
+            const float2 ov = *reinterpret_cast<const float2*>(&o[t][2 * lane]);
+            const float ms = sum64(ov.x * ov.x + ov.y * ov.y) * (1.0f / D);
+            const float rr = frsqrt(ms + p.norm_eps);
+            const float gx = z[i].x * sigmoid_fast(z[i].x);
+            const float gy = z[i].y * sigmoid_fast(z[i].y);
+            const float2 y = make_float2(ov.x * rr * wn.x * gx, ov.y * rr * wn.y * gy);
+            store_pair<OUT>(p.out, rows[i] * p.o_st + h * p.o_sh + 2 * lane, y);
+        }
+    }
+}
+
 template <int ACT, int ST, int OUT>
 __global__ void __launch_bounds__(MT) __attribute__((amdgpu_waves_per_eu(2)))
 gdn_prefill_mma_kernel(const PParams p)
@@ -478,14 +497,20 @@ gdn_prefill_mma_kernel(const PParams p)
     const float dtb = p.dt_bias[h];
     const float2 wn = *reinterpret_cast<const float2*>(p.norm_weight + 2 * lane);
 
+    // The gated RMSNorm of a sub-chunk runs while the next sub-chunk's
+    // matrix products do: its tokens' rows, z and count stay in registers.
+    float2 zc[MTW];
+    int64_t rc[MTW];
+    int nprev = 0;
     for (int pos = 0; pos < L;) {
         const int n = sub_len(pos, L, p.chunk);
         const int next = pos + n;
         MRaw<ACT> raw;
         issue_sub<ACT>(p, c0, L, pos, wave, lane, h, kh, raw);
+        float2 zn[MTW];
+        int64_t rn[MTW];
 
         // ---- stage: normalised k and q, v, gates; z stays in registers ----
-        float2 zc[MTW];
 #pragma unroll
         for (int i = 0; i < MTW; ++i) {
             const int t = wave + 4 * i;
@@ -497,7 +522,8 @@ gdn_prefill_mma_kernel(const PParams p)
             const float rk = live ? frsqrt(nk + 1e-6f) : 0.0f;
             const float rq = live ? p.scale * frsqrt(nq + 1e-6f) : 0.0f;
             const float2 vv = unpack_pair<ACT>(raw.v[i]);
-            zc[i] = unpack_pair<ACT>(raw.z[i]);
+            zn[i] = unpack_pair<ACT>(raw.z[i]);
+            rn[i] = raw.row[i];
             *reinterpret_cast<float2*>(&sm.x[t][2 * lane]) =
                 live ? make_float2(kv.x * rk, kv.y * rk) : make_float2(0.0f, 0.0f);
             *reinterpret_cast<float2*>(&sm.x[MC + t][2 * lane]) =
@@ -505,7 +531,6 @@ gdn_prefill_mma_kernel(const PParams p)
             *reinterpret_cast<float2*>(&sm.v[t][2 * lane]) =
                 live ? vv : make_float2(0.0f, 0.0f);
             if (lane == 0) {
-                sm.row[t] = raw.row[i];
                 const float x = unpack_one<ACT>(raw.a[i]) + dtb;
                 sm.g[t] = live ? A * softplus_fast(x) : 0.0f;
                 sm.beta[t] = live ? sigmoid_fast(unpack_one<ACT>(raw.b[i])) : 0.0f;
@@ -550,6 +575,14 @@ gdn_prefill_mma_kernel(const PParams p)
                                                       0, 0, 0);
         }
         __builtin_amdgcn_s_setprio(0);
+        // the previous sub-chunk's gated RMSNorm, while the products run
+        epilogue<OUT>(p, sm.o, zc, rc, nprev, wave, lane, h, wn);
+#pragma unroll
+        for (int i = 0; i < MTW; ++i) {
+            zc[i] = zn[i];
+            rc[i] = rn[i];
+        }
+        nprev = n;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int i = 8 * (r / 4) + 4 * lh + r % 4;
@@ -557,15 +590,15 @@ gdn_prefill_mma_kernel(const PParams p)
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            sm.u.gp[wave >> 1][gcol][4 * lq + r][l16] = Gm[r];
+            sm.gp[wave >> 1][gcol][4 * lq + r][l16] = Gm[r];
         __syncthreads();
 
         // ---- decay-weighted Gram coefficients (one (i, t) pair per thread) ----
         {
             const int i = tid / MC, t = tid % MC;
             const float Gi = sm.G[i], Gt = sm.G[t], Ge = sm.G[MC - 1];
-            const float kk = sm.u.gp[0][0][i][t] + sm.u.gp[1][0][i][t];
-            const float kq = sm.u.gp[0][1][i][t] + sm.u.gp[1][1][i][t];
+            const float kk = sm.gp[0][0][i][t] + sm.gp[1][0][i][t];
+            const float kq = sm.gp[0][1][i][t] + sm.gp[1][1][i][t];
             const float e = i <= t ? fexp(Gt - Gi) : 0.0f;
             sm.akk[t][i] = i < t ? e * kk : 0.0f;
             sm.bkq[t][i] = e * kq;
@@ -600,7 +633,7 @@ gdn_prefill_mma_kernel(const PParams p)
 #pragma unroll
             for (int i = 0; i < MC; ++i)
                 o = fmaf(sm.bkq[t][i], d[i], o);
-            sm.u.o[t][vrow] = o;
+            sm.o[t][vrow] = o;
         }
 
         // ---- S <- e^{G_end} S + D' K^T ----
@@ -634,24 +667,9 @@ gdn_prefill_mma_kernel(const PParams p)
         }
         __syncthreads();
 
-        // ---- gated RMSNorm over V per (token, head) ----
-#pragma unroll
-        for (int i = 0; i < MTW; ++i) {
-            const int t = wave + 4 * i;
-            if (t < n) {
-                const float2 o = *reinterpret_cast<const float2*>(&sm.u.o[t][2 * lane]);
-                const int64_t row = sm.row[t];
-                const float ms = sum64(o.x * o.x + o.y * o.y) * (1.0f / D);
-                const float rr = frsqrt(ms + p.norm_eps);
-                const float gx = zc[i].x * sigmoid_fast(zc[i].x);
-                const float gy = zc[i].y * sigmoid_fast(zc[i].y);
-                const float2 y = make_float2(o.x * rr * wn.x * gx, o.y * rr * wn.y * gy);
-                store_pair<OUT>(p.out, row * p.o_st + h * p.o_sh + 2 * lane, y);
-            }
-        }
-        __syncthreads();
         pos = next;
     }
+    epilogue<OUT>(p, sm.o, zc, rc, nprev, wave, lane, h, wn);
 
     // ---- the final state, rounded once, written once ----
 #pragma unroll
