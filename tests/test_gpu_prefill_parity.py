@@ -192,12 +192,15 @@ def test_full_size_sampled(dev, name, seqs):
             assert torch.equal(gp[s], b.pool[s])
 
 
-def test_fp8_state_saturates(dev):
+@pytest.mark.parametrize("chunk", [8, 16])
+def test_fp8_state_saturates(dev, chunk):
     """An FP8 pool whose chunk-end states run past the E4M3 range: the
     carry is saturated to +-448 at every chunk end (about 10% of the final
-    state here), as in the oracle."""
+    state here), as in the oracle -- in the token recurrence (chunk 8) and
+    in the chunkwise kernel (chunk 16)."""
     b = workloads.prefill_batch(lens=[40, 23], HK=1, HV=4, act="f32", state="f8", out="f32",
-                                chunk_size=8, init_frac=1.0, num_slots=3, pool_std=120, seed=47)
+                                chunk_size=chunk, init_frac=1.0, num_slots=3, pool_std=120,
+                                seed=47)
     b.pool = b.pool.float().nan_to_num(0.0).clamp(-448, 448).to(torch.float8_e4m3fn)
     b.v = b.v * 5000.0
     gp, go = check(b, dev)
