@@ -317,7 +317,8 @@ gdn_prefill_kernel(const PParams p)
 // -- the token recurrence unrolled, the same values up to rounding order.
 // The products S0 [k^ | q^] (V x K by K x 2MC) and the update
 // S <- e^{G_end} S + D' K^T (D'_i = e^{G_end - G_i} d_i) run on
-// v_mfma_f32_32x32x2f32; the MC x MC triangular solve for d runs on the
+// v_mfma_f32_32x32x2f32, the k^ rows of the Gram matrix on
+// v_mfma_f32_16x16x4f32; the MC x MC triangular solve for d runs on the
 // vector ALU, one value row per lane.
 //
 // Layout: wave w owns value rows v = 32w..32w+31.  The state is kept
