@@ -59,6 +59,14 @@ KERNEL_SOURCES = {
 SHARED_SOURCES = ["gdn_internal.h", "dtype_cvt.h"]
 
 
+def pools_to_cycle(pool_bytes: int, requested=None) -> int:
+    """Layers (state pools) the gdn path cycles: as requested, else at least
+    four and at least MIN_CYCLED_POOL_BYTES in all."""
+    if requested:
+        return requested
+    return max(DEFAULT_LAYERS["gdn"], -(-MIN_CYCLED_POOL_BYTES // pool_bytes))
+
+
 def kernel_source_hash(path: str = "gdn") -> str:
     """Hash of the sources that build the kernel of ``path``."""
     h = hashlib.sha256()
@@ -286,8 +294,7 @@ def main():
     kw = ops.batch_args(batch, dev)
     kw["out"] = torch.zeros((batch.n_tok, batch.HV, batch.V), dtype=batch.out_dtype, device=dev)
     pool_bytes = batch.pool.numel() * batch.pool.element_size()
-    if not layers_given:
-        args.layers = max(args.layers, -(-MIN_CYCLED_POOL_BYTES // pool_bytes))
+    args.layers = pools_to_cycle(pool_bytes, layers_given)
     pools = [kw["state"]] + [kw["state"].clone() for _ in range(args.layers - 1)]
     tokens = batch.draft_tokens()
     alg_bytes = batch.algorithmic_bytes()
