@@ -111,7 +111,8 @@ typedef struct {
  * With n_tok == 0 the activation/output pointers may be NULL and every call
  * is a no-op.
  * Alignment: q, k, v, z, out data pointers aligned to 2 elements and their
- * token/head strides even; A_log, dt_bias, norm_weight 4-byte aligned. */
+ * token/head strides even; A_log and dt_bias 4-byte aligned; norm_weight
+ * 8-byte aligned (the kernels read it in pairs). */
 typedef struct {
     gdn_view q, k, v, z, a, b, out;
     const float* A_log;
@@ -170,6 +171,12 @@ gdn_status gdn_spec_decode_update(const gdn_layer* layer,
  * and writing slot state_indices[i] in place (a negative slot marks padding:
  * skipped, its output row untouched).  token_indx int32 [num_tokens] or NULL
  * gives the row of entry i (NULL: row = i).  Same recurrence with L = 1.
+ * Defined by: #46090 实现拆解 item 1 (a batch without speculative decoding
+ * takes the non-spec path, _cpu_gdn_attention_nonspec, one state slot per
+ * request) and #52191 实现拆解 item 3 (the decode kernel
+ * fused_sigmoid_gating_delta_rule_update reads its slot as state_t, updates
+ * in FP32 and writes the same slot back); #51812 关键源码片段 (the non-spec
+ * rows are gathered by non_spec_token_indx, the gates with them).
  */
 gdn_status gdn_decode_update(const gdn_layer* layer, const gdn_state_pool* pool,
                              const int32_t* state_indices, int32_t num_tokens,
@@ -221,7 +228,10 @@ gdn_status gdn_prefill_update(const gdn_layer* layer, const gdn_state_pool* pool
 /*
  * Host-side check of prefill metadata on HOST copies: cu_seqlens
  * non-decreasing from 0, slots < num_slots (negative = skipped) and
- * distinct, rows inside [0, n_tok) and used once.
+ * distinct, rows inside [0, n_tok) and used once.  The prefill kernels trust
+ * this metadata as the decode kernels trust theirs; #46090 评论区精华 and
+ * 风险与影响 record the state-index arrays left unvalidated there, which
+ * this check covers for the prefill.
  */
 gdn_status gdn_validate_prefill_indices_host(int64_t num_slots, int64_t n_tok,
                                              const int32_t* cu_seqlens, int32_t num_seqs,
@@ -229,6 +239,12 @@ gdn_status gdn_validate_prefill_indices_host(int64_t num_slots, int64_t n_tok,
                                              const int32_t* token_indx);
 
 /*
+ * Defined by #46090 评论区精华 and 风险与影响: static analysis of the CPU spec
+ * kernel found the acc - 1 underflow (fixed by the clamp) and noted that
+ * spec_state_indices is never checked for shape or range.  The kernels keep
+ * trusting device metadata (and skip a unit whose metadata is out of
+ * range); this is the check a caller runs on host copies instead.
+ *
  * Host-side check of the metadata contract on HOST copies of the index
  * arrays (any pointer may be NULL when its count is 0; the token-index arrays
  * may be NULL for the identity).  Returns GDN_OK, or GDN_ERR_INVALID with the
@@ -259,10 +275,17 @@ gdn_status gdn_validate_indices_host(int64_t num_slots, int64_t n_tok,
 gdn_status gdn_cast_to_state(const float* src, void* dst, int64_t n, int32_t dtype,
                              hipStream_t stream);
 
-/* Reason for the last non-OK status returned on this thread ("" if none). */
+/* Reason for the last non-OK status returned on this thread ("" if none).
+ * Defined by #51674 实现拆解 item 3: _fused_gdn_decode_unsupported_reason
+ * gathers every constraint of the fused kernel (non-interleaved GQA,
+ * K = V = 128, dtypes, at most 8 MTP tokens) into one reason string, and an
+ * explicit request that fails them raises instead of falling back.  Here a
+ * call that fails a check returns GDN_ERR_UNSUPPORTED or GDN_ERR_INVALID and
+ * this returns the reason; there is no fallback path. */
 const char* gdn_last_error(void);
 
-/* Static name of a status code. */
+/* Static name of a status code (the same #51674 passage: the status is the
+ * raise-or-proceed decision, this is its name for logs). */
 const char* gdn_status_string(gdn_status status);
 
 /* GDN_ABI_VERSION of the built library, and the sizes of the argument

@@ -102,8 +102,11 @@ gdn_status check_layer(const gdn_layer* L)
     }
     if (!L->A_log || !L->dt_bias || !L->norm_weight)
         return fail(GDN_ERR_INVALID, "A_log, dt_bias and norm_weight must be non-NULL");
-    if (!aligned(L->A_log, 4) || !aligned(L->dt_bias, 4) || !aligned(L->norm_weight, 4))
-        return fail(GDN_ERR_INVALID, "A_log, dt_bias and norm_weight must be 4-byte aligned");
+    if (!aligned(L->A_log, 4) || !aligned(L->dt_bias, 4))
+        return fail(GDN_ERR_INVALID, "A_log and dt_bias must be 4-byte aligned");
+    // the kernels read norm_weight as float pairs
+    if (!aligned(L->norm_weight, 8))
+        return fail(GDN_ERR_INVALID, "norm_weight must be 8-byte aligned");
     if (!(L->norm_eps >= 0.0f))
         return fail(GDN_ERR_INVALID, "norm_eps must be >= 0");
     return GDN_OK;

@@ -507,3 +507,113 @@ def make(name: str, **overrides) -> GDNBatch:
     if kind == "mixed":
         return mixed_batch(name=name, **cfg)
     return spec_batch(name=name, **cfg)
+
+
+@dataclass
+class PostConvBatch:
+    """One decode step from the packed projections through the conv update
+    with rewind and the recurrent update (CPU tensors).
+
+    ``x`` [n_tok, C] is the packed q/k/v projection before the conv, C =
+    2 HK K + HV V in the order q, k, v; the conv writes its output into one
+    buffer of the same shape, which the recurrent update reads as three
+    strided views.  ``zba`` [n_tok, HV V + 2 HV] packs the output gate z and
+    the gate inputs b, a, read as views too (never split into copies).
+    Spec sequence b owns conv line ``conv_lines[b]``; single-token entry i
+    owns ``ns_conv_lines[i]``; both take their rows through the gather
+    indices when those are given."""
+    name: str
+    HK: int
+    HV: int
+    K: int
+    V: int
+    x: torch.Tensor                     # [n_tok, C]
+    zba: torch.Tensor                   # [n_tok, HV V + 2 HV]
+    conv_weight: torch.Tensor           # [C, width] fp32
+    conv_bias: torch.Tensor             # [C] fp32
+    conv_cache: torch.Tensor            # [num_lines, state_len, C]
+    A_log: torch.Tensor
+    dt_bias: torch.Tensor
+    norm_weight: torch.Tensor
+    pool: torch.Tensor                  # [num_slots, HV, V, K]
+    cu_seqlens: torch.Tensor            # int32 [B+1]
+    spec_state_indices: torch.Tensor    # int32 [B, T]
+    num_accepted_tokens: torch.Tensor   # int32 [B]
+    conv_lines: torch.Tensor            # int32 [B]
+    spec_token_indx: Optional[torch.Tensor] = None
+    state_indices: Optional[torch.Tensor] = None
+    ns_conv_lines: Optional[torch.Tensor] = None
+    non_spec_token_indx: Optional[torch.Tensor] = None
+    T: int = 0
+    scale: float = 0.0
+    norm_eps: float = 1e-5
+
+    @property
+    def n_tok(self) -> int:
+        return self.x.shape[0]
+
+    @property
+    def num_seqs(self) -> int:
+        return self.cu_seqlens.shape[0] - 1
+
+
+def postconv_batch(*, n_spec, T, n_non_spec=0, HK, HV, K=128, V=128, act="bf16",
+                   state="bf16", width=4, acc_lo=0, acc_hi=None, gather=None, pool_std=0.05,
+                   seed=0, name="postconv") -> PostConvBatch:
+    """A decode step of n_spec sequences of T draft rows and n_non_spec
+    single tokens.  With gather (default: when there are single tokens) the
+    units are laid out in random order and both parts reach their rows
+    through gather indices, as in a mixed batch.
+
+    Draw order: x, zba ~ N(0, 1); conv weight, bias ~ U(-0.5, 0.5); A_log ~
+    U(-1, 1), dt_bias ~ U(-0.5, 0.5), norm_weight ~ U(0.5, 1.5); the conv
+    buffer ~ N(0, 1) line by line; the pool ~ N(0, pool_std) slot by slot;
+    the line permutation, the slot permutation, num_accepted ~
+    U{acc_lo..acc_hi}; the unit order."""
+    acc_hi = T if acc_hi is None else acc_hi
+    gather = n_non_spec > 0 if gather is None else gather
+    C = 2 * HK * K + HV * V
+    n_tok = n_spec * T + n_non_spec
+    num_lines = n_spec + n_non_spec
+    num_slots = n_spec * T + n_non_spec
+    state_len = width - 2 + T
+    rng = np.random.Generator(np.random.PCG64(seed))
+    act_t = _DT[act]
+    x = _draw_act(rng, (n_tok, C), act_t)
+    zba = _draw_act(rng, (n_tok, HV * V + 2 * HV), act_t)
+    cw = torch.from_numpy(rng.uniform(-0.5, 0.5, (C, width)).astype(np.float32))
+    cb = torch.from_numpy(rng.uniform(-0.5, 0.5, C).astype(np.float32))
+    A_log = torch.from_numpy(rng.uniform(-1.0, 1.0, HV).astype(np.float32))
+    dt_bias = torch.from_numpy(rng.uniform(-0.5, 0.5, HV).astype(np.float32))
+    w = torch.from_numpy(rng.uniform(0.5, 1.5, V).astype(np.float32))
+    cache = torch.empty((num_lines, state_len, C), dtype=act_t)
+    for ln in range(num_lines):
+        cache[ln] = _draw_act(rng, (state_len, C), act_t)
+    pool = _draw_pool(rng, num_slots, HV, V, K, pool_std, _DT[state])
+    lines = rng.permutation(num_lines).astype(np.int32)
+    slots = rng.permutation(num_slots).astype(np.int32)
+    acc = rng.integers(acc_lo, acc_hi + 1, size=n_spec).astype(np.int32)
+    spec_rows, ns_rows = list(range(n_spec * T)), list(range(n_spec * T, n_tok))
+    if gather:
+        spec_rows, ns_rows, row = [], [], 0
+        for u in rng.permutation(n_spec + n_non_spec):
+            if u < n_non_spec:
+                ns_rows.append(row)
+                row += 1
+            else:
+                spec_rows.extend(range(row, row + T))
+                row += T
+    cu = np.arange(0, (n_spec + 1) * T, T, dtype=np.int32)
+    ns = n_non_spec > 0
+    return PostConvBatch(
+        name=name, HK=HK, HV=HV, K=K, V=V, x=x, zba=zba, conv_weight=cw, conv_bias=cb,
+        conv_cache=cache, A_log=A_log, dt_bias=dt_bias, norm_weight=w, pool=pool,
+        cu_seqlens=torch.from_numpy(cu),
+        spec_state_indices=torch.from_numpy(slots[:n_spec * T].reshape(n_spec, T).copy()),
+        num_accepted_tokens=torch.from_numpy(acc),
+        conv_lines=torch.from_numpy(lines[:n_spec].copy()),
+        spec_token_indx=torch.tensor(spec_rows, dtype=torch.int32) if gather else None,
+        state_indices=torch.from_numpy(slots[n_spec * T:].copy()) if ns else None,
+        ns_conv_lines=torch.from_numpy(lines[n_spec:].copy()) if ns else None,
+        non_spec_token_indx=torch.tensor(ns_rows, dtype=torch.int32) if ns else None,
+        T=T, scale=K ** -0.5)

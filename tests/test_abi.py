@@ -109,6 +109,9 @@ def test_valid_empty_batch_is_a_no_op(lib):
     (lambda L, P: setattr(L.v, "stride_tok", 257), 1, "misaligned"),
     (lambda L, P: setattr(L.a, "stride_head", 2), 1, "stride_head"),
     (lambda L, P: setattr(L, "A_log", None), 1, "A_log"),
+    # a float32 slice such as w[1:] is contiguous but only 4-byte aligned;
+    # the kernels read norm_weight in pairs
+    (lambda L, P: setattr(L, "norm_weight", L.norm_weight + 4), 1, "norm_weight must be 8-byte"),
     (lambda L, P: setattr(L, "norm_eps", -1.0), 1, "norm_eps"),
     (lambda L, P: setattr(P, "data", P.data + 8), 1, "16-byte"),
     (lambda L, P: setattr(P, "num_slots", 0), 1, "num_slots"),
@@ -327,3 +330,15 @@ def test_prefill_entry_errors_and_validator(lib):
         ops.validate_prefill_indices(b.pool.shape[0], b.n_tok, b.cu_seqlens, b.state_indices,
                                      token_indx=tix)
     assert "used twice" in ei.value.reason
+
+
+def test_offset_norm_weight_view_is_rejected(lib):
+    """w[1:] of a float32 tensor passes the binding's contiguity check but is
+    only 4-byte aligned; the library rejects it before enqueueing anything."""
+    layer, pool, keep = _layer_and_pool()
+    w = torch.ones(129)[1:]
+    assert w.is_contiguous() and w.data_ptr() % 8 == 4
+    q, k, v, z, a, b, out, A_log, dt = keep[:9]
+    layer = ops.make_layer(q, k, v, z, a, b, A_log, dt, w, out)
+    assert _spec(lib, layer, pool) == 1
+    assert "norm_weight must be 8-byte" in ops.last_error()

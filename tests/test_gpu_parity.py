@@ -10,8 +10,9 @@ output, state atol/rtol 3e-2), tightened for FP32 state:
   * state: |s_gpu - s_orc| <= atol + rtol |s_orc| with atol = rtol = 1e-5 for
     FP32 state and 3e-2 for BF16/FP16 state.
 Full-size workloads run in the benchmark's launch configuration; the oracle
-checks a sample of their sequences, and the touched-set / untouched-byte
-checks cover the whole pool.
+checks every sequence (on host threads), the touched-set / untouched-byte
+checks cover the whole pool, and for 8/16-bit pools the stored elements that
+round differently from the oracle are counted and bounded.
 """
 import copy
 
@@ -21,15 +22,11 @@ import torch
 
 import oracle
 from speculative_decode_amd import ops, workloads
-from _helpers import bitwise_equal, rel_l2, slots_touched
+from _helpers import (F8_TOL, STATE_TOL, bitwise_equal, compare_states_on_device,
+                      oracle_spec_parts, rel_l2, slots_touched)
 
 pytestmark = pytest.mark.gpu
 
-STATE_TOL = {torch.float32: 1e-5, torch.bfloat16: 3e-2, torch.float16: 3e-2}
-# FP8 E4M3 state: one unit in the last place -- spacing 2^-9 below 2^-6,
-# |x| 2^-3 above: a value the GPU (fp32) and the oracle (double) place on
-# opposite sides of a rounding boundary may land one step apart.
-F8_TOL = (2.0 ** -9, 2.0 ** -3)
 OUT_REL_L2 = 5e-4
 
 
@@ -315,62 +312,14 @@ def test_out_of_range_metadata_skips_the_unit(dev):
 
 
 # --------------------------------------------------------------------------
-# full-size workloads: sampled oracle + whole-pool byte checks
+# full-size workloads: every sequence against the oracle + whole-pool byte checks
 # --------------------------------------------------------------------------
-def sample_batch(batch, seqs):
-    """Compact oracle batch holding only the sampled sequences, their rows and
-    their slots; returns it with the original slot ids of its pool."""
-    cu = batch.cu_seqlens.tolist()
-    rows, lens, slots = [], [], []
-    for bi in seqs:
-        rr = list(range(cu[bi], cu[bi + 1]))
-        if batch.spec_token_indx is not None:
-            rr = [int(batch.spec_token_indx[g]) for g in rr]
-        rows += rr
-        lens.append(len(rr))
-        acc = int(batch.num_accepted_tokens[bi])
-        slots += [int(batch.spec_state_indices[bi, max(acc - 1, 0)])]
-        slots += batch.spec_state_indices[bi, :len(rr)].tolist()
-    slots = sorted(set(slots))
-    remap = {s: i for i, s in enumerate(slots)}
-    sb = copy.copy(batch)
-    sb.q, sb.k, sb.v, sb.z, sb.a, sb.b = (x[rows] for x in
-                                          (batch.q, batch.k, batch.v, batch.z, batch.a, batch.b))
-    sb.cu_seqlens = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32)
-    T = batch.spec_state_indices.shape[1]
-    sb.spec_state_indices = torch.tensor(
-        [[remap.get(int(s), 0) for s in batch.spec_state_indices[bi]] for bi in seqs],
-        dtype=torch.int32).reshape(len(seqs), T)
-    # entries past each sequence's length are never read or written; any
-    # in-range value will do (0) -- but the rewind entry must map exactly
-    for k, bi in enumerate(seqs):
-        acc = int(batch.num_accepted_tokens[bi])
-        j = max(acc - 1, 0)
-        sb.spec_state_indices[k, j] = remap[int(batch.spec_state_indices[bi, j])]
-    sb.num_accepted_tokens = batch.num_accepted_tokens[list(seqs)].clone()
-    sb.spec_token_indx = None
-    sb.state_indices = None
-    sb.non_spec_token_indx = None
-    sb.pool = batch.pool[slots]
-    return sb, slots, rows
-
-
-def pick_sequences(batch, k=6):
-    """A few sequences of a large batch: the first, the last, the middle, and
-    the lowest and highest acceptance counts present (acc = 0 if any)."""
-    acc = batch.num_accepted_tokens.tolist()
-    picks = {0, batch.num_seqs - 1, batch.num_seqs // 2, acc.index(min(acc)),
-             acc.index(max(acc))}
-    if 1 in acc:
-        picks.add(acc.index(1))
-    return sorted(picks)[:k]
-
-
-def check_sampled(name, dev):
+def check_whole(name, dev, *, threads=16):
+    """A full-size workload in the benchmark's launch configuration, every
+    sequence compared with the oracle (run on host threads)."""
     batch = workloads.make(name)
-    seqs = pick_sequences(batch)
     print(f"[{name}] generated: B={batch.num_seqs} T={batch.T} pool={tuple(batch.pool.shape)} "
-          f"{batch.pool.dtype}; oracle on sequences {seqs}", flush=True)
+          f"{batch.pool.dtype}", flush=True)
     args = ops.batch_args(batch, dev)
     before = args["state"].clone()
     args["out"] = torch.zeros((batch.n_tok, batch.HV, batch.V), dtype=batch.out_dtype, device=dev)
@@ -378,24 +327,24 @@ def check_sampled(name, dev):
     torch.cuda.synchronize()
     assert touched_slots_dev(before, args["state"]) == expected_slots(batch)
     del before
-    rows_all = processed_rows(batch)
-    assert len(rows_all) == batch.n_tok
-    sb, slots, rows = sample_batch(batch, seqs)
-    po, oo = run_oracle(sb)
-    written = sorted(set(sum((sb.spec_state_indices[k, :int(sb.cu_seqlens[k + 1] - sb.cu_seqlens[k])]
-                              .tolist() for k in range(len(seqs))), [])))
-    for s in written:
-        assert_state_close(args["state"][slots[s]].cpu(), po[s], batch.pool.dtype,
-                           f"{name} slot {slots[s]}")
+    assert len(processed_rows(batch)) == batch.n_tok
+    written, states, rows, outs = oracle_spec_parts(
+        batch.q, batch.k, batch.v, batch.z, batch.a, batch.b, batch.A_log, batch.dt_bias,
+        batch.norm_weight, batch.pool, batch.cu_seqlens, batch.spec_state_indices,
+        batch.num_accepted_tokens, token_indx=batch.spec_token_indx,
+        out_dtype=batch.out_dtype, scale=batch.scale, norm_eps=batch.norm_eps, threads=threads)
+    assert sorted(written) == expected_slots(batch)
+    print(f"[{name}] oracle done on all {batch.num_seqs} sequences", flush=True)
+    compare_states_on_device(args["state"], written, states, batch.pool.dtype, name)
     err = rel_l2(out[torch.tensor(rows, device=dev)].cpu().double().numpy(),
-                 oo.double().numpy())
+                 outs.double().numpy())
     assert err < OUT_REL_L2, f"{name}: output rel L2 {err:.3e}"
-    print(f"[{name}] sampled {len(seqs)} sequences: out rel L2 {err:.2e}", flush=True)
+    print(f"[{name}] all {batch.num_seqs} sequences: out rel L2 {err:.2e}", flush=True)
 
 
 @pytest.mark.parametrize("name", ["mtp_b128_f32", "mtp_b128_bf16", "large_b512_f16"])
-def test_full_size_sampled(dev, name):
-    check_sampled(name, dev)
+def test_full_size_whole(dev, name):
+    check_whole(name, dev)
 
 
 # --------------------------------------------------------------------------
@@ -508,8 +457,8 @@ def test_fp8_state_mixed(dev):
     check_full(b, dev)
 
 
-def test_fp8_full_size_sampled(dev):
-    check_sampled("mtp_b128_f8", dev)
+def test_fp8_full_size_whole(dev):
+    check_whole("mtp_b128_f8", dev)
 
 
 def test_fp8_state_saturates_and_keeps_nan(dev):
@@ -571,3 +520,27 @@ def test_random_configurations(dev, i):
         perm = r.permutation(b.n_tok).astype(np.int32)
         b.spec_token_indx = torch.from_numpy(perm)
     check_full(b, dev)
+
+
+def test_softplus_threshold_branch(dev):
+    """a + dt_bias > 20 takes the linear branch softplus(x) = x (threshold
+    20) in the kernel as in the oracle; A_log = -4 keeps the decay alpha
+    near 0.6, so the branch decides the state and the output.  Half of the
+    heads sit above the threshold, half below it."""
+    b = workloads.spec_batch(B=4, T=5, HK=2, HV=8, act="f32", state="f32", acc_lo=0,
+                             acc_hi=5, seed=41)
+    g = torch.Generator().manual_seed(41)
+    b.a = b.a.clone()
+    b.a[:, :4] = 22.0 + 8.0 * torch.rand((b.n_tok, 4), generator=g)
+    b.dt_bias = b.dt_bias.clone()
+    b.dt_bias[:4] = 0.0
+    b.A_log = torch.full_like(b.A_log, -4.0)
+    assert float((b.a[:, :4] + b.dt_bias[:4]).min()) > 20.0
+    assert float((b.a[:, 4:] + b.dt_bias[4:]).max()) < 20.0
+    check_full(b, dev)
+    bb = copy.copy(b)
+    bb.pool = b.pool.to(torch.bfloat16)
+    bb.q, bb.k, bb.v, bb.z, bb.a, bb.b = (x.to(torch.bfloat16)
+                                          for x in (b.q, b.k, b.v, b.z, b.a, b.b))
+    bb.out_dtype = torch.bfloat16
+    check_full(bb, dev)

@@ -163,33 +163,57 @@ def test_deterministic(dev):
     assert torch.equal(p1, p2) and torch.equal(o1, o2)
 
 
-@pytest.mark.parametrize("name,seqs", [("prefill_b16_l2048", [0, 11]),
-                                       ("prefill_ragged_b32", [3, 17, 30])])
-def test_full_size_sampled(dev, name, seqs):
-    """The benchmark's batch and launch; the oracle on a few whole sequences
-    (every head), the rest checked for touching nothing outside their slots."""
-    b = workloads.make_prefill(name)
-    gp, go = run_gpu(b, dev)
+def oracle_each_sequence(b, threads=16):
+    """The prefill oracle on every sequence of a large batch, one oracle call
+    per sequence on host threads (each with its own rows and a one-slot
+    pool; the calls share nothing).  Returns {slot: state}, rows, outputs."""
+    from concurrent.futures import ThreadPoolExecutor
+
     cu = b.cu_seqlens.tolist()
-    sub_rows = torch.tensor([r for i in seqs for r in range(cu[i], cu[i + 1])], dtype=torch.int32)
-    sub_cu = torch.zeros(len(seqs) + 1, dtype=torch.int32)
-    sub_cu[1:] = torch.cumsum(torch.tensor([cu[i + 1] - cu[i] for i in seqs]), 0)
-    hi = None if b.has_initial_state is None else b.has_initial_state[seqs]
-    op, oo = oracle.prefill_update(b.q, b.k, b.v, b.z, b.a, b.b, b.A_log, b.dt_bias,
-                                   b.norm_weight, b.pool, sub_cu, b.state_indices[seqs],
-                                   has_initial_state=hi, token_indx=sub_rows,
-                                   chunk_size=b.chunk_size, out_dtype=b.out_dtype)
-    tol = STATE_TOL[b.pool.dtype]
-    for i in seqs:
+    oracle.round_to(torch.float32, [0.0])          # load the library before the threads
+
+    def one(i):
+        rows = torch.arange(cu[i], cu[i + 1], dtype=torch.int32)
+        if b.token_indx is not None:
+            rows = b.token_indx[cu[i]:cu[i + 1]].clone()
         s = int(b.state_indices[i])
-        d = (gp[s].double() - op[s].double()).abs()
-        assert (d <= tol + tol * op[s].double().abs()).all(), (i, d.max())
-    rows = sub_rows.long()
-    assert rel_l2(go[rows].double(), oo[rows].double()) < OUT_REL_L2
+        hi = None if b.has_initial_state is None else b.has_initial_state[i:i + 1]
+        r = rows.long()
+        p, o = oracle.prefill_update(b.q[r], b.k[r], b.v[r], b.z[r], b.a[r], b.b[r], b.A_log,
+                                     b.dt_bias, b.norm_weight, b.pool[s:s + 1],
+                                     torch.tensor([0, len(rows)], dtype=torch.int32),
+                                     torch.zeros(1, dtype=torch.int32), has_initial_state=hi,
+                                     chunk_size=b.chunk_size, scale=b.scale,
+                                     norm_eps=b.norm_eps, out_dtype=b.out_dtype)
+        return s, p[0], r, o
+
+    live = [i for i in range(b.num_seqs) if cu[i + 1] > cu[i] and int(b.state_indices[i]) >= 0]
+    with ThreadPoolExecutor(threads) as ex:
+        res = list(ex.map(one, live))
+    return ({s: p for s, p, _, _ in res}, torch.cat([r for _, _, r, _ in res]),
+            torch.cat([o for _, _, _, o in res]))
+
+
+@pytest.mark.parametrize("name", ["prefill_b16_l2048", "prefill_ragged_b32"])
+def test_full_size_whole(dev, name):
+    """The benchmark's batch and launch; the oracle on every sequence (every
+    head), and every slot no sequence owns unchanged."""
+    b = workloads.make_prefill(name)
+    print(f"[{name}] {b.num_seqs} sequences, {b.n_tok} tokens", flush=True)
+    gp, go = run_gpu(b, dev)
+    states, rows, outs = oracle_each_sequence(b)
+    print(f"[{name}] oracle done", flush=True)
+    atol, rtol = tols(b.pool.dtype)
+    for s, st in states.items():
+        d = (gp[s].double() - st.double()).abs()
+        assert (d <= atol + rtol * st.double().abs()).all(), (s, d.max())
+    err = rel_l2(go[rows].double(), outs.double())
+    assert err < OUT_REL_L2, err
     used = set(b.state_indices.tolist())
     for s in range(b.pool.shape[0]):
         if s not in used:
             assert torch.equal(gp[s], b.pool[s])
+    print(f"[{name}] all sequences: out rel L2 {err:.2e}", flush=True)
 
 
 @pytest.mark.parametrize("chunk", [8, 16])

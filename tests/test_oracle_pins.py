@@ -153,6 +153,34 @@ def test_p13_dense_form(K, V, HK, HV, B, T, seed):
             np.testing.assert_allclose(out[row, h].numpy(), y, rtol=1e-10, atol=1e-13)
 
 
+@pytest.mark.parametrize("seed", [0, 1])
+def test_p13_softplus_threshold_branch(seed):
+    """softplus_threshold (#46090 spec-kernel arguments, value not printed;
+    read as 20): for a + dt_bias > 20 the oracle takes softplus(x) = x.  The
+    dense form keeps the closed-form gate (1 + e^x)^(-e^A_log), which differs
+    from exp(-e^A_log x) by a relative e^A_log * e^-x < 1e-12 here -- so the
+    branch must return x itself (not 0, not e^x, not log1p of an overflowed
+    exponential).  A_log = -4 keeps alpha near 0.6 so the decay is visible."""
+    bt = with_pool_dtype(tiny(K=8, V=8, HK=1, HV=2, B=2, T=3, seed=seed), F64)
+    bt.q, bt.k, bt.v, bt.z = (x.double() for x in (bt.q, bt.k, bt.v, bt.z))
+    g = torch.Generator().manual_seed(seed)
+    bt.a = (24.0 + 6.0 * torch.rand(bt.a.shape, generator=g, dtype=F64))
+    bt.dt_bias = torch.zeros(bt.HV, dtype=F64)
+    bt.A_log = torch.full((bt.HV,), -4.0, dtype=F64)
+    assert float((bt.a + bt.dt_bias[None]).min()) > 20.0
+    pool, out = orc_spec(bt, out_dtype=F64)
+    p0 = bt.pool.numpy()
+    for bi in range(bt.num_seqs):
+        slots, outs = dense_sequence(bt, p0, bi)
+        for (s_, h), S in slots.items():
+            np.testing.assert_allclose(pool[s_, h].numpy(), S, rtol=1e-11, atol=1e-13)
+        for (row, h), y in outs.items():
+            np.testing.assert_allclose(out[row, h].numpy(), y, rtol=1e-10, atol=1e-13)
+    # the decay is in effect: alpha is neither 0 nor 1
+    alpha = np.exp(-np.exp(-4.0) * bt.a.numpy())
+    assert 0.4 < alpha.min() and alpha.max() < 0.7
+
+
 # --------------------------------------------------------------------------
 # Slot semantics (#46090 spec kernel: clamp, skip, per-token store;
 # #51674 item 1: rewind to the last accepted slot, store every token).
