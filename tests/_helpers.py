@@ -169,15 +169,17 @@ F8_TOL = (2.0 ** -9, 2.0 ** -3)
 # Stored tiles of a 8/16-bit pool against the oracle's rounding.  The kernel
 # carries the state in FP32 and the oracle in double, so where the exact
 # value lies within the FP32 error of a rounding boundary the two round to
-# neighbouring values; elsewhere the bits agree.  Measured share of
-# differing elements at full size (B=128/512, T=8): see STEP_SHARE_BOUND.
-# Where a stored value is tiny next to the tile's other values, the FP32
-# error of the cancellation that produced it can span more than one step:
-# the one-step rule applies above STEP_FLOOR, the element-wise bar below.
+# neighbouring values; elsewhere the bits agree.  Measured at full size
+# (every stored element of mtp_b128_bf16, large_b512_f16, mtp_b128_f8): 6.8e-5
+# of BF16, 3.4e-4 of FP16 and 8e-7 of FP8 elements differ, each by one step.
+# The bounds below are about three times those shares.  Where a stored value
+# is tiny next to the tile's other values, the FP32 error of the cancellation
+# that produced it can span more than one step: the one-step rule applies
+# above STEP_FLOOR, the element-wise bar below it.
 STEP_FLOOR = {torch.bfloat16: 2.0 ** -12, torch.float16: 2.0 ** -10,
               torch.float8_e4m3fn: 2.0 ** -6}
-STEP_SHARE_BOUND = {torch.bfloat16: 2e-3, torch.float16: 2e-3,
-                    torch.float8_e4m3fn: 2e-3}
+STEP_SHARE_BOUND = {torch.bfloat16: 2e-4, torch.float16: 1e-3,
+                    torch.float8_e4m3fn: 5e-6}
 
 
 def compare_states_on_device(gpu_pool, written, states, dtype, what, *, chunk=64,
