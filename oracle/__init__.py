@@ -112,6 +112,51 @@ def _prepare(q, k, v, z, a, b, A_log, dt_bias, norm_weight, pool, out, out_dtype
             (n_tok, HK, HV, K, V))
 
 
+class PreparedCall:
+    """One oracle call with its arguments already marshalled: ``run()``
+    executes only the C function (so that it can be timed alone) and
+    ``result()`` converts the written pool and output back to tensors."""
+
+    def __init__(self, fn_name, args, keep, what, finish):
+        self._fn_name, self._args, self._what, self._finish = fn_name, args, what, finish
+        self._keep = keep           # the arrays the marshalled pointers refer to
+
+    def run(self):
+        rc = getattr(_load(), self._fn_name)(*self._args)
+        if rc:
+            raise ValueError(f"oracle {self._what}: {_ERR.get(rc, rc)}")
+        return self
+
+    def result(self):
+        return self._finish()
+
+
+def _tensors_back(pool64, pool_dtype, out64, out_dtype):
+    return lambda: (torch.from_numpy(pool64).to(pool_dtype), torch.from_numpy(out64).to(out_dtype))
+
+
+def prepare_spec_update(q, k, v, z, a, b, A_log, dt_bias, norm_weight, pool,
+                        cu_seqlens, spec_state_indices, num_accepted_tokens, *,
+                        token_indx=None, out=None, out_dtype=None, scale=None,
+                        norm_eps=1e-5) -> PreparedCall:
+    """spec_update's arguments marshalled for the C call (see spec_update)."""
+    arrs, out64, odt, pool64, (n_tok, HK, HV, K, V) = _prepare(
+        q, k, v, z, a, b, A_log, dt_bias, norm_weight, pool, out, out_dtype)
+    cu = _i32(cu_seqlens)
+    si = _i32(spec_state_indices)
+    na = _i32(num_accepted_tokens)
+    ti = _i32(token_indx)
+    B = cu.shape[0] - 1
+    stride = si.shape[1] if si.ndim == 2 else max(1, si.shape[0] // max(B, 1))
+    scale = K ** -0.5 if scale is None else scale
+    args = (*[_p(x) for x in arrs], _p(out64), _FMT[odt], _p(pool64), _FMT[pool.dtype],
+            pool.shape[0], n_tok, _p(cu), B, _p(si), stride, _p(na), _p(ti),
+            HK, HV, K, V, float(scale), float(norm_eps))
+    keep = (arrs, cu, si, na, ti, out64, pool64)
+    return PreparedCall("orc_spec_update", args, keep,
+                        "spec_update", _tensors_back(pool64, pool.dtype, out64, odt))
+
+
 def spec_update(q, k, v, z, a, b, A_log, dt_bias, norm_weight, pool,
                 cu_seqlens, spec_state_indices, num_accepted_tokens, *,
                 token_indx=None, out=None, out_dtype=None, scale=None,
@@ -122,42 +167,57 @@ def spec_update(q, k, v, z, a, b, A_log, dt_bias, norm_weight, pool,
     ``[B, spec_stride]``; ``out`` (default zeros) supplies the rows that are
     not processed.  Inputs are not modified.
     """
+    return prepare_spec_update(q, k, v, z, a, b, A_log, dt_bias, norm_weight, pool, cu_seqlens,
+                               spec_state_indices, num_accepted_tokens, token_indx=token_indx,
+                               out=out, out_dtype=out_dtype, scale=scale,
+                               norm_eps=norm_eps).run().result()
+
+
+def prepare_decode_update(q, k, v, z, a, b, A_log, dt_bias, norm_weight, pool,
+                          state_indices, *, token_indx=None, out=None, out_dtype=None,
+                          scale=None, norm_eps=1e-5) -> PreparedCall:
+    """decode_update's arguments marshalled for the C call (see decode_update)."""
     arrs, out64, odt, pool64, (n_tok, HK, HV, K, V) = _prepare(
         q, k, v, z, a, b, A_log, dt_bias, norm_weight, pool, out, out_dtype)
-    cu = _i32(cu_seqlens)
-    si = _i32(spec_state_indices)
-    na = _i32(num_accepted_tokens)
+    si = _i32(state_indices)
     ti = _i32(token_indx)
-    B = cu.shape[0] - 1
-    stride = si.shape[1] if si.ndim == 2 else max(1, si.shape[0] // max(B, 1))
     scale = K ** -0.5 if scale is None else scale
-    rc = _load().orc_spec_update(
-        *[_p(x) for x in arrs], _p(out64), _FMT[odt], _p(pool64), _FMT[pool.dtype],
-        pool.shape[0], n_tok, _p(cu), B, _p(si), stride, _p(na), _p(ti),
-        HK, HV, K, V, float(scale), float(norm_eps))
-    if rc:
-        raise ValueError(f"oracle spec_update: {_ERR.get(rc, rc)}")
-    return (torch.from_numpy(pool64).to(pool.dtype),
-            torch.from_numpy(out64).to(odt))
+    args = (*[_p(x) for x in arrs], _p(out64), _FMT[odt], _p(pool64), _FMT[pool.dtype],
+            pool.shape[0], n_tok, _p(si), si.shape[0], _p(ti),
+            HK, HV, K, V, float(scale), float(norm_eps))
+    keep = (arrs, si, ti, out64, pool64)
+    return PreparedCall("orc_decode_update", args, keep,
+                        "decode_update", _tensors_back(pool64, pool.dtype, out64, odt))
 
 
 def decode_update(q, k, v, z, a, b, A_log, dt_bias, norm_weight, pool,
                   state_indices, *, token_indx=None, out=None, out_dtype=None,
                   scale=None, norm_eps=1e-5):
     """Non-speculative single-token in-place update; returns new tensors."""
+    return prepare_decode_update(q, k, v, z, a, b, A_log, dt_bias, norm_weight, pool,
+                                 state_indices, token_indx=token_indx, out=out,
+                                 out_dtype=out_dtype, scale=scale,
+                                 norm_eps=norm_eps).run().result()
+
+
+def prepare_prefill_update(q, k, v, z, a, b, A_log, dt_bias, norm_weight, pool, cu_seqlens,
+                           state_indices, *, has_initial_state=None, token_indx=None,
+                           chunk_size=64, out=None, out_dtype=None, scale=None,
+                           norm_eps=1e-5) -> PreparedCall:
+    """prefill_update's arguments marshalled for the C call."""
     arrs, out64, odt, pool64, (n_tok, HK, HV, K, V) = _prepare(
         q, k, v, z, a, b, A_log, dt_bias, norm_weight, pool, out, out_dtype)
+    cu = _i32(cu_seqlens)
     si = _i32(state_indices)
+    hi = _i32(has_initial_state)
     ti = _i32(token_indx)
     scale = K ** -0.5 if scale is None else scale
-    rc = _load().orc_decode_update(
-        *[_p(x) for x in arrs], _p(out64), _FMT[odt], _p(pool64), _FMT[pool.dtype],
-        pool.shape[0], n_tok, _p(si), si.shape[0], _p(ti),
-        HK, HV, K, V, float(scale), float(norm_eps))
-    if rc:
-        raise ValueError(f"oracle decode_update: {_ERR.get(rc, rc)}")
-    return (torch.from_numpy(pool64).to(pool.dtype),
-            torch.from_numpy(out64).to(odt))
+    args = (*[_p(x) for x in arrs], _p(out64), _FMT[odt], _p(pool64), _FMT[pool.dtype],
+            pool.shape[0], n_tok, _p(cu), cu.shape[0] - 1, _p(si), _p(hi), _p(ti),
+            int(chunk_size), HK, HV, K, V, float(scale), float(norm_eps))
+    keep = (arrs, cu, si, hi, ti, out64, pool64)
+    return PreparedCall("orc_prefill_update", args, keep,
+                        "prefill_update", _tensors_back(pool64, pool.dtype, out64, odt))
 
 
 def prefill_update(q, k, v, z, a, b, A_log, dt_bias, norm_weight, pool, cu_seqlens,
@@ -166,28 +226,18 @@ def prefill_update(q, k, v, z, a, b, A_log, dt_bias, norm_weight, pool, cu_seqle
     """Chunked prefill: one slot per sequence, the state rounded to the pool
     dtype after every chunk_size-th token and after the last; returns
     ``(pool_after, out_after)`` as new tensors."""
-    arrs, out64, odt, pool64, (n_tok, HK, HV, K, V) = _prepare(
-        q, k, v, z, a, b, A_log, dt_bias, norm_weight, pool, out, out_dtype)
-    cu = _i32(cu_seqlens)
-    si = _i32(state_indices)
-    hi = _i32(has_initial_state)
-    ti = _i32(token_indx)
-    scale = K ** -0.5 if scale is None else scale
-    rc = _load().orc_prefill_update(
-        *[_p(x) for x in arrs], _p(out64), _FMT[odt], _p(pool64), _FMT[pool.dtype],
-        pool.shape[0], n_tok, _p(cu), cu.shape[0] - 1, _p(si), _p(hi), _p(ti),
-        int(chunk_size), HK, HV, K, V, float(scale), float(norm_eps))
-    if rc:
-        raise ValueError(f"oracle prefill_update: {_ERR.get(rc, rc)}")
-    return (torch.from_numpy(pool64).to(pool.dtype),
-            torch.from_numpy(out64).to(odt))
+    return prepare_prefill_update(q, k, v, z, a, b, A_log, dt_bias, norm_weight, pool,
+                                  cu_seqlens, state_indices,
+                                  has_initial_state=has_initial_state, token_indx=token_indx,
+                                  chunk_size=chunk_size, out=out, out_dtype=out_dtype,
+                                  scale=scale, norm_eps=norm_eps).run().result()
 
 
 CONV_ACT = {None: 0, "none": 0, "silu": 1}
 
 
-def _conv_call(x, weight, bias, cache, cu, lines, num_acc, token_indx, out, out_dtype,
-               activation, B):
+def _conv_prepare(x, weight, bias, cache, cu, lines, num_acc, token_indx, out, out_dtype,
+                  activation, B) -> PreparedCall:
     n_tok, C = x.shape
     num_lines, state_len, C2 = cache.shape
     Cw, width = weight.shape
@@ -198,13 +248,22 @@ def _conv_call(x, weight, bias, cache, cu, lines, num_acc, token_indx, out, out_
     x64, w64 = _f64(x), _f64(weight)
     b64 = None if bias is None else _f64(bias)
     out64, cache64 = _f64(out).copy(), _f64(cache).copy()
-    rc = _load().orc_conv_update(
-        _p(x64), _p(out64), _FMT[odt], _p(cache64), _FMT[cache.dtype], num_lines, state_len,
-        n_tok, C, width, _p(w64), _p(b64), CONV_ACT[activation], _p(cu), B, _p(lines),
-        _p(num_acc), _p(token_indx))
-    if rc:
-        raise ValueError(f"oracle conv update: {_ERR.get(rc, rc)}")
-    return torch.from_numpy(cache64).to(cache.dtype), torch.from_numpy(out64).to(odt)
+    args = (_p(x64), _p(out64), _FMT[odt], _p(cache64), _FMT[cache.dtype], num_lines, state_len,
+            n_tok, C, width, _p(w64), _p(b64), CONV_ACT[activation], _p(cu), B, _p(lines),
+            _p(num_acc), _p(token_indx))
+    keep = (x64, w64, b64, cu, lines, num_acc, token_indx, out64, cache64)
+    return PreparedCall("orc_conv_update", args, keep,
+                        "conv update", _tensors_back(cache64, cache.dtype, out64, odt))
+
+
+def prepare_conv_spec_update(x, weight, bias, cache, cu_seqlens, conv_indices,
+                             num_accepted_tokens, *, token_indx=None, out=None, out_dtype=None,
+                             activation="silu") -> PreparedCall:
+    """conv_spec_update's arguments marshalled for the C call."""
+    cu = _i32(cu_seqlens)
+    return _conv_prepare(x, weight, bias, cache, cu, _i32(conv_indices),
+                         _i32(num_accepted_tokens), _i32(token_indx), out, out_dtype,
+                         activation, cu.shape[0] - 1)
 
 
 def conv_spec_update(x, weight, bias, cache, cu_seqlens, conv_indices, num_accepted_tokens,
@@ -216,15 +275,14 @@ def conv_spec_update(x, weight, bias, cache, cu_seqlens, conv_indices, num_accep
     ``conv_indices[b]`` is the buffer line of sequence b.  Inputs are not
     modified.
     """
-    cu = _i32(cu_seqlens)
-    return _conv_call(x, weight, bias, cache, cu, _i32(conv_indices),
-                      _i32(num_accepted_tokens), _i32(token_indx), out, out_dtype, activation,
-                      cu.shape[0] - 1)
+    return prepare_conv_spec_update(x, weight, bias, cache, cu_seqlens, conv_indices,
+                                    num_accepted_tokens, token_indx=token_indx, out=out,
+                                    out_dtype=out_dtype, activation=activation).run().result()
 
 
 def conv_decode_update(x, weight, bias, cache, conv_indices, *, token_indx=None, out=None,
                        out_dtype=None, activation="silu"):
     """Non-speculative single-token conv update (a negative line is padding)."""
     lines = _i32(conv_indices)
-    return _conv_call(x, weight, bias, cache, None, lines, None, _i32(token_indx), out,
-                      out_dtype, activation, lines.shape[0])
+    return _conv_prepare(x, weight, bias, cache, None, lines, None, _i32(token_indx), out,
+                         out_dtype, activation, lines.shape[0]).run().result()

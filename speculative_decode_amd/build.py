@@ -25,20 +25,25 @@ def hipcc() -> str:
     return path
 
 
-def command(out: str) -> list:
-    return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-            # packed-FP32 VALU forms are kept out of the generated code
-            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            # fused multiply-adds only where the source writes fmaf: every
-            # instantiation then rounds the same expression the same way
-            "-ffp-contract=off",
-            "-Wall", "-Wno-unused-command-line-argument",
-            "-o", out] + SOURCES
+FLAGS = ["-O3", "-std=c++17", "-fPIC",
+         # packed-FP32 VALU forms are kept out of the generated code
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # fused multiply-adds only where the source writes fmaf: every
+         # instantiation then rounds the same expression the same way
+         "-ffp-contract=off",
+         "-Wall", "-Wno-unused-command-line-argument"]
+OBJDIR = os.path.join(HERE, "_build")
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = command(tmp)
+def compile_command(src: str, obj: str) -> list:
+    return [hipcc(), f"--offload-arch={ARCH}"] + FLAGS + ["-c", src, "-o", obj]
+
+
+def link_command(objs: list, out: str) -> list:
+    return [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", out] + objs
+
+
+def _run(cmd: list, verbose: bool):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -50,6 +55,19 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs), file=sys.stderr)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source (in parallel, one hipcc per file) and link the
+    shared library; always recompiles."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    os.makedirs(OBJDIR, exist_ok=True)
+    objs = [os.path.join(OBJDIR, os.path.basename(src) + ".o") for src in SOURCES]
+    with ThreadPoolExecutor(len(SOURCES)) as ex:
+        list(ex.map(lambda so: _run(compile_command(*so), verbose), zip(SOURCES, objs)))
+    tmp = LIB + ".tmp"
+    _run(link_command(objs, tmp), verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -3,6 +3,7 @@
 
 #include "../../include/gdn_conv.h"
 #include "../../include/gdn_spec.h"
+#include "../../include/gdn_bench.h"
 
 namespace gdn {
 

@@ -542,6 +542,243 @@ __global__ void __launch_bounds__(256) cast_kernel(const float* src, void* dst, 
     }
 }
 
+// ---- the launch's traffic pattern, with no arithmetic ------------------------
+// For measurement only.  The same grid, unit mapping, metadata phase and
+// per-CU block count as gdn_update_kernel, and the same HBM traffic: the
+// rewind tile read once (16-byte non-temporal loads, same lane layout) and
+// written back unchanged to each draft-token slot (non-temporal stores, same
+// order), the q/k/v/z rows and the gate scalars read, the out rows written
+// (with the XOR of the bits read, so that no load is dead).  Nothing is
+// computed, so its duration is what the memory system allows for exactly
+// that traffic -- the ceiling the kernel is measured against.
+// ASZ, SSZ, OSZ: bytes per activation, state and output element.
+template <int ASZ, int SSZ, int OSZ, bool SPEC>
+__global__ void __launch_bounds__(NTHREADS) gdn_traffic_kernel(const KParams p)
+{
+    constexpr int CH = D * SSZ / 128;
+    constexpr int EPC = 16 / SSZ;
+    constexpr int CSTRIDE = D / CH;
+    constexpr int NT = SPEC ? MAXT : 1;
+    constexpr int NTW = (NT + 3) / 4;
+    using raw_t = typename std::conditional<ASZ == 4, uint2, uint32_t>::type;
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int g = lane >> 3;
+    const int j = lane & 7;
+
+    const uint32_t nblk = gridDim.x;
+    const uint32_t xcd = blockIdx.x % NXCD;
+    const uint32_t per = nblk / NXCD, rem = nblk % NXCD;
+    const uint32_t unit = xcd * per + (xcd < rem ? xcd : rem) + blockIdx.x / NXCD;
+    const uint32_t entry32 = unit / static_cast<uint32_t>(p.HV);
+    const int64_t entry = entry32;
+    const int h = static_cast<int>(unit - entry32 * static_cast<uint32_t>(p.HV));
+    const int kh = static_cast<int>(static_cast<uint32_t>(h) / static_cast<uint32_t>(p.group));
+
+    bool spec_unit = SPEC;
+    int64_t seq = entry;
+    if (SPEC && p.num_ns > 0) {
+        const int64_t E = p.num_spec + p.num_ns;
+        const int64_t before = entry * p.num_spec / E;
+        const int64_t after = (entry + 1) * p.num_spec / E;
+        spec_unit = after > before;
+        seq = spec_unit ? before : entry - before;
+    }
+    int L;
+    int64_t c0, rslot;
+    int64_t wslot[NT];
+    const int32_t* tix = p.tix;
+    if (spec_unit) {
+        c0 = p.cu[seq];
+        L = static_cast<int>(p.cu[seq + 1] - c0);
+        const int acc = p.num_acc[seq];
+        if (L <= 0 || L > MAXT || L > p.spec_stride || acc < 0 || acc > p.spec_stride)
+            return;
+        const int32_t* sidx = p.spec_idx + seq * p.spec_stride;
+        rslot = sidx[acc > 1 ? acc - 1 : 0];
+        bool bad = rslot < 0 || rslot >= p.num_slots;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int tt = t < L ? t : L - 1;
+            wslot[t] = sidx[tt];
+            const int64_t row = p.tix ? p.tix[c0 + tt] : c0 + tt;
+            bad |= wslot[t] < 0 || wslot[t] >= p.num_slots || row < 0 || row >= p.n_tok;
+        }
+        if (bad)
+            return;
+    } else {
+        tix = SPEC ? p.ns_tix : p.tix;
+        rslot = p.state_idx[seq];
+        c0 = seq;
+        L = 1;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            wslot[t] = rslot;
+        const int64_t row = tix ? tix[seq] : seq;
+        if (rslot < 0 || rslot >= p.num_slots || row < 0 || row >= p.n_tok)
+            return;
+    }
+
+    // the activation rows of this wave's tokens, as the kernel loads them
+    raw_t x[NTW];
+    int64_t rowv[NTW];
+#pragma unroll
+    for (int i = 0; i < NTW; ++i) {
+        const int t = wave + 4 * i;
+        const int tt = t < L ? t : L - 1;
+        const int64_t row = tix ? tix[c0 + tt] : c0 + tt;
+        rowv[i] = row;
+        const char* qa = static_cast<const char*>(p.q) + (row * p.q_st + kh * p.q_sh + 2 * lane) * ASZ;
+        const char* ka = static_cast<const char*>(p.k) + (row * p.k_st + kh * p.k_sh + 2 * lane) * ASZ;
+        const char* va = static_cast<const char*>(p.v) + (row * p.v_st + h * p.v_sh + 2 * lane) * ASZ;
+        const char* za = static_cast<const char*>(p.z) + (row * p.z_st + h * p.z_sh + 2 * lane) * ASZ;
+        x[i] = *reinterpret_cast<const raw_t*>(qa);
+        raw_t kx = *reinterpret_cast<const raw_t*>(ka);
+        raw_t vx = *reinterpret_cast<const raw_t*>(va);
+        raw_t zx = *reinterpret_cast<const raw_t*>(za);
+        uint32_t ab;
+        if constexpr (ASZ == 4)
+            ab = static_cast<const uint32_t*>(p.a)[row * p.a_st + h] ^
+                 static_cast<const uint32_t*>(p.b)[row * p.b_st + h];
+        else
+            ab = static_cast<const uint16_t*>(p.a)[row * p.a_st + h] ^
+                 static_cast<const uint16_t*>(p.b)[row * p.b_st + h];
+        if constexpr (ASZ == 4) {
+            x[i].x ^= kx.x ^ vx.x ^ zx.x ^ ab;
+            x[i].y ^= kx.y ^ vx.y ^ zx.y;
+        } else {
+            x[i] ^= kx ^ vx ^ zx ^ ab;
+        }
+    }
+
+    // the rewind tile, read once
+    const size_t tile = static_cast<size_t>(D) * D;
+    const char* rbase = static_cast<const char*>(p.pool) +
+                        (static_cast<size_t>(rslot) * p.HV + h) * tile * SSZ;
+    u32x4 raw[RPT][CH];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+        const int row = wave * ROWS_PER_WAVE + r * 8 + g;
+#pragma unroll
+        for (int c = 0; c < CH; ++c)
+            raw[r][c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+                rbase + (static_cast<size_t>(row) * D + c * CSTRIDE + j * EPC) * SSZ));
+    }
+
+    // ... written back unchanged to every draft-token slot
+    char* pool = static_cast<char*>(p.pool);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        if (t >= L)
+            break;
+        __builtin_amdgcn_sched_barrier(0);
+        char* wbase = pool + (static_cast<size_t>(wslot[t]) * p.HV + h) * tile * SSZ;
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
+            const int row = wave * ROWS_PER_WAVE + r * 8 + g;
+#pragma unroll
+            for (int c = 0; c < CH; ++c)
+                __builtin_nontemporal_store(raw[r][c], reinterpret_cast<u32x4*>(
+                    wbase + (static_cast<size_t>(row) * D + c * CSTRIDE + j * EPC) * SSZ));
+        }
+    }
+
+    // the out rows
+#pragma unroll
+    for (int i = 0; i < NTW; ++i) {
+        const int t = wave + 4 * i;
+        if (t < L) {
+            char* oa = static_cast<char*>(p.out) +
+                       (rowv[i] * p.o_st + h * p.o_sh + 2 * lane) * OSZ;
+            uint32_t lo;
+            if constexpr (ASZ == 4)
+                lo = x[i].x ^ x[i].y;
+            else
+                lo = x[i];
+            if constexpr (OSZ == 4)
+                *reinterpret_cast<uint2*>(oa) = make_uint2(lo, lo);
+            else
+                *reinterpret_cast<uint32_t*>(oa) = lo;
+        }
+    }
+}
+
+// Blocks per CU of the kernel whose traffic the pattern reproduces, and the
+// dynamic LDS that gives the pattern kernel (whose registers would allow
+// more) the same count.
+template <int A, int S, int O, bool SPEC>
+hipError_t traffic_lds(const KParams& p, size_t* lds)
+{
+    size_t real_lds = 0;
+    hipError_t e = plan_lds<SPEC ? MAXT : 1>(p.max_writes, S, &real_lds);
+    if (e != hipSuccess)
+        return e;
+    int n = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &n, reinterpret_cast<const void*>(&gdn_update_kernel<A, S, O, SPEC>), NTHREADS, real_lds);
+    if (e != hipSuccess)
+        return e;
+    DeviceInfo d;
+    if ((e = device_info(&d)) != hipSuccess)
+        return e;
+    *lds = 0;
+    const size_t share = static_cast<size_t>(d.lds_per_cu) / (n + 1) + 1;
+    if (n > 0 && share <= static_cast<size_t>(d.lds_per_block))
+        *lds = share;
+    return hipSuccess;
+}
+
+constexpr int esize(int dt) { return dt == GDN_F32 ? 4 : (dt == GDN_F8E4M3 ? 1 : 2); }
+
+template <int A, int S, int O, bool SPEC>
+hipError_t launch_traffic_typed(const KParams& p, int64_t grid, hipStream_t stream)
+{
+    size_t lds = 0;
+    hipError_t e = traffic_lds<A, S, O, SPEC>(p, &lds);
+    if (e != hipSuccess)
+        return e;
+    KParams args = p;
+    void* argv[] = {&args};
+    return hipLaunchKernel(
+        reinterpret_cast<const void*>(
+            &gdn_traffic_kernel<esize(A), esize(S), esize(O), SPEC>),
+        dim3(static_cast<uint32_t>(grid)), dim3(NTHREADS), argv, lds, stream);
+}
+
+template <int A, int S, bool SPEC>
+hipError_t launch_traffic_out(int out, const KParams& p, int64_t grid, hipStream_t s)
+{
+    switch (out) {
+    case GDN_F32: return launch_traffic_typed<A, S, GDN_F32, SPEC>(p, grid, s);
+    case GDN_F16: return launch_traffic_typed<A, S, GDN_F16, SPEC>(p, grid, s);
+    default: return launch_traffic_typed<A, S, GDN_BF16, SPEC>(p, grid, s);
+    }
+}
+
+template <int A, bool SPEC>
+hipError_t launch_traffic_state(int st, int out, const KParams& p, int64_t grid, hipStream_t s)
+{
+    switch (st) {
+    case GDN_F32: return launch_traffic_out<A, GDN_F32, SPEC>(out, p, grid, s);
+    case GDN_F16: return launch_traffic_out<A, GDN_F16, SPEC>(out, p, grid, s);
+    case GDN_F8E4M3: return launch_traffic_out<A, GDN_F8E4M3, SPEC>(out, p, grid, s);
+    default: return launch_traffic_out<A, GDN_BF16, SPEC>(out, p, grid, s);
+    }
+}
+
+template <bool SPEC>
+hipError_t launch_traffic(int act, int st, int out, const KParams& p, int64_t grid,
+                          hipStream_t s)
+{
+    switch (act) {
+    case GDN_F32: return launch_traffic_state<GDN_F32, SPEC>(st, out, p, grid, s);
+    case GDN_F16: return launch_traffic_state<GDN_F16, SPEC>(st, out, p, grid, s);
+    default: return launch_traffic_state<GDN_BF16, SPEC>(st, out, p, grid, s);
+    }
+}
+
 gdn_status device_status(hipError_t e)
 {
     if (e == hipSuccess)
@@ -693,4 +930,61 @@ extern "C" gdn_status gdn_cast_to_state(const float* src, void* dst, int64_t n, 
     default: fn = reinterpret_cast<const void*>(&cast_kernel<GDN_F8E4M3>); break;
     }
     return device_status(hipLaunchKernel(fn, dim3(grid), dim3(256), argv, 0, stream));
+}
+
+extern "C" gdn_status gdn_traffic_pattern(const gdn_layer* layer, const gdn_state_pool* pool,
+                                          const int32_t* cu_seqlens, int32_t num_seqs,
+                                          int32_t max_q_len, const int32_t* spec_state_indices,
+                                          int32_t spec_stride,
+                                          const int32_t* num_accepted_tokens,
+                                          const int32_t* spec_token_indx,
+                                          const int32_t* state_indices, int32_t num_tokens,
+                                          const int32_t* non_spec_token_indx, hipStream_t stream)
+{
+    gdn::clear_error();
+    gdn_status st;
+    if ((st = gdn::check_layer(layer)) != GDN_OK || (st = gdn::check_pool(pool)) != GDN_OK)
+        return st;
+    if (num_seqs < 0 || num_tokens < 0)
+        return gdn::fail(GDN_ERR_INVALID, "num_seqs or num_tokens is negative");
+    if (max_q_len < 1)
+        return gdn::fail(GDN_ERR_INVALID, "max_q_len must be >= 1");
+    if (max_q_len > GDN_MAX_DRAFT_TOKENS)
+        return gdn::fail(GDN_ERR_UNSUPPORTED, "max_q_len %d exceeds %d draft tokens",
+                         max_q_len, GDN_MAX_DRAFT_TOKENS);
+    if (spec_stride < 1)
+        return gdn::fail(GDN_ERR_INVALID, "spec_stride must be >= 1");
+    if ((num_seqs == 0 && num_tokens == 0) || layer->n_tok == 0)
+        return GDN_OK;
+    if (num_seqs > 0 && (!cu_seqlens || !spec_state_indices || !num_accepted_tokens))
+        return gdn::fail(GDN_ERR_INVALID, "spec metadata pointer is NULL");
+    if (num_tokens > 0 && !state_indices)
+        return gdn::fail(GDN_ERR_INVALID, "state_indices is NULL");
+    const int64_t grid =
+        (static_cast<int64_t>(num_seqs) + num_tokens) * layer->num_v_heads;
+    if (grid > 0x7fffffffLL)
+        return gdn::fail(GDN_ERR_INVALID, "(num_seqs + num_tokens) * num_v_heads exceeds the "
+                                          "grid limit");
+    KParams p = make_params(layer, pool);
+    p.spec_stride = spec_stride;
+    if (num_seqs == 0) {
+        // the single-token launch of gdn_decode_update
+        p.state_idx = state_indices;
+        p.tix = non_spec_token_indx;
+        p.spec_stride = 1;
+        p.max_writes = 1;
+        return device_status(launch_traffic<false>(layer->act_dtype, pool->dtype,
+                                                   layer->out_dtype, p, grid, stream));
+    }
+    p.cu = cu_seqlens;
+    p.spec_idx = spec_state_indices;
+    p.num_acc = num_accepted_tokens;
+    p.tix = spec_token_indx;
+    p.num_spec = num_seqs;
+    p.state_idx = state_indices;
+    p.ns_tix = non_spec_token_indx;
+    p.num_ns = num_tokens;
+    p.max_writes = max_q_len;
+    return device_status(launch_traffic<true>(layer->act_dtype, pool->dtype, layer->out_dtype,
+                                              p, grid, stream));
 }

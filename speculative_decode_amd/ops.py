@@ -118,6 +118,9 @@ SIGNATURES = {
     "gdn_validate_conv_indices_host": (ctypes.c_int, [_I64, _I32, _I32, _I64, _VP, _I32, _I32,
                                                       _VP, _VP, _VP, _VP, _I32, _VP]),
     "gdn_conv_abi_struct_sizes": (None, [ctypes.POINTER(ctypes.c_size_t)] * 2),
+    "gdn_traffic_pattern": (ctypes.c_int, [ctypes.POINTER(GdnLayer),
+                                           ctypes.POINTER(GdnStatePool), _VP, _I32, _I32, _VP,
+                                           _I32, _VP, _VP, _VP, _I32, _VP, _VP]),
 }
 
 
@@ -382,6 +385,39 @@ def forward_core(q, k, v, z, a, b, A_log, dt_bias, norm_weight, state, *,
         decode_update(q, k, v, z, a, b, A_log, dt_bias, norm_weight, state,
                       non_spec_state_indices, token_indx=non_spec_token_indx, out=out,
                       scale=scale, norm_eps=norm_eps)
+    return out
+
+
+def traffic_pattern(q, k, v, z, a, b, A_log, dt_bias, norm_weight, state, *,
+                    spec_cu_seqlens=None, spec_state_indices=None, num_accepted_tokens=None,
+                    spec_token_indx=None, non_spec_state_indices=None,
+                    non_spec_token_indx=None, out=None, scale=None, norm_eps=1e-5,
+                    max_q_len=MAX_DRAFT_TOKENS, single_launch=True):
+    """The HBM traffic of the forward_core launch with the same arguments and
+    no arithmetic (gdn_traffic_pattern, include/gdn_bench.h): a measurement
+    of the memory system's ceiling for that traffic.  Overwrites the written
+    slots of ``state`` with copies of the rewind tiles and ``out`` with
+    meaningless bits.  ``single_launch`` is accepted for symmetry with
+    forward_core; a mixed batch is always one launch here."""
+    lib = load_library()
+    if out is None:
+        out = torch.zeros_like(z)
+    dev = q.device
+    layer = make_layer(q, k, v, z, a, b, A_log, dt_bias, norm_weight, out,
+                       scale=scale, norm_eps=norm_eps)
+    pool = make_pool(state, layer, dev)
+    has_spec = spec_cu_seqlens is not None and spec_cu_seqlens.shape[0] > 1
+    cu = _meta(spec_cu_seqlens, "cu_seqlens", dev) if has_spec else None
+    si = _meta(spec_state_indices, "spec_state_indices", dev) if has_spec else None
+    na = _meta(num_accepted_tokens, "num_accepted_tokens", dev) if has_spec else None
+    st = _meta(spec_token_indx, "spec_token_indx", dev) if has_spec else None
+    ns = _meta(non_spec_state_indices, "state_indices", dev)
+    nst = _meta(non_spec_token_indx, "non_spec_token_indx", dev)
+    B = cu.shape[0] - 1 if has_spec else 0
+    _check(lib.gdn_traffic_pattern(ctypes.byref(layer), ctypes.byref(pool), _ptr(cu), B,
+                                   int(max_q_len), _ptr(si), si.shape[1] if has_spec else 1,
+                                   _ptr(na), _ptr(st), _ptr(ns),
+                                   0 if ns is None else ns.shape[0], _ptr(nst), _stream(dev)))
     return out
 
 

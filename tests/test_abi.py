@@ -342,3 +342,18 @@ def test_offset_norm_weight_view_is_rejected(lib):
     layer = ops.make_layer(q, k, v, z, a, b, A_log, dt, w, out)
     assert _spec(lib, layer, pool) == 1
     assert "norm_weight must be 8-byte" in ops.last_error()
+
+
+def test_traffic_pattern_argument_errors(lib):
+    """The measurement entry runs the same host checks as the update entries
+    and enqueues nothing when they fail (CPU tensors: no device call)."""
+    layer, pool, keep = _layer_and_pool()
+    m = torch.zeros(16, dtype=torch.int32)
+    p = ctypes.c_void_p(m.data_ptr())
+    call = lambda L, B, maxq, ns: lib.gdn_traffic_pattern(   # noqa: E731
+        ctypes.byref(L), ctypes.byref(pool), p, B, maxq, p, 4, p, None, p, ns, None, None)
+    assert call(layer, 0, 4, 0) == 0                         # nothing to do
+    assert call(layer, 1, 9, 0) == 2 and "exceeds" in ops.last_error()
+    assert call(layer, -1, 4, 0) == 1
+    layer.norm_weight = layer.norm_weight + 4
+    assert call(layer, 1, 4, 0) == 1 and "norm_weight" in ops.last_error()

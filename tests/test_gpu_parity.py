@@ -544,3 +544,38 @@ def test_softplus_threshold_branch(dev):
                                           for x in (b.q, b.k, b.v, b.z, b.a, b.b))
     bb.out_dtype = torch.bfloat16
     check_full(bb, dev)
+
+
+@pytest.mark.parametrize("name", ["mtp_b32", "mixed_b128", "decode_b128"])
+def test_traffic_pattern_moves_the_launch_bytes(dev, name):
+    """The measurement launch (include/gdn_bench.h) touches exactly the
+    kernel's bytes: every draft slot receives a copy of its unit's rewind
+    tile, every other slot is unchanged, and only processed out rows are
+    written."""
+    b = workloads.make(name)
+    args = ops.batch_args(b, dev)
+    before = args["state"].clone()
+    args["out"] = torch.zeros((b.n_tok, b.HV, b.V), dtype=b.out_dtype, device=dev)
+    ops.traffic_pattern(**args)
+    torch.cuda.synchronize()
+    after = args["state"]
+    want = expected_slots(b)
+    # a slot rewritten with its own tile (in-place entries, and the write at
+    # t = acc - 1) keeps its bytes: the changed slots are a subset
+    assert set(touched_slots_dev(before, after)) <= set(want)
+    lens = (b.cu_seqlens[1:] - b.cu_seqlens[:-1]).tolist()
+    for bi, L in enumerate(lens):
+        acc = int(b.num_accepted_tokens[bi])
+        r = int(b.spec_state_indices[bi, max(acc - 1, 0)])
+        for t in range(L):
+            assert torch.equal(after[int(b.spec_state_indices[bi, t])], before[r])
+    keep = torch.ones(b.pool.shape[0], dtype=torch.bool)
+    keep[want] = False
+    assert torch.equal(after[keep.to(dev)], before[keep.to(dev)])
+    if b.state_indices is not None:
+        for s in b.state_indices.tolist():
+            if s >= 0:
+                assert torch.equal(after[s], before[s])       # in place, unchanged
+    rows = processed_rows(b)
+    other = [r for r in range(b.n_tok) if r not in set(rows)]
+    assert (args["out"][other] == 0).all() if other else True
