@@ -94,6 +94,17 @@ struct Step {
     int64_t row[TS];
 };
 
+// A block barrier that orders LDS only.  The waves of a block exchange
+// everything through LDS; __syncthreads() would also wait for every global
+// load still in flight, so the activation loads issued a step ahead would
+// cost a full memory latency at the next barrier.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // The raw activations of one step for one wave (tokens wave, wave + NWAVES, ...).
 template <int ACT>
 struct StepRaw {
@@ -224,7 +235,7 @@ gdn_prefill_kernel(const PParams p)
         // ---- the next step's loads, in flight during this step's tokens ----
         if (step + 1 < nsteps)
             issue_step<ACT>(p, c0, L, step + 1, wave, lane, h, kh, raw);
-        __syncthreads();
+        lds_barrier();
 
         // ---- the step's tokens, strictly in order ----
         for (int tl = 0; tl < n; ++tl) {
@@ -275,7 +286,7 @@ gdn_prefill_kernel(const PParams p)
                         round_pair<ST>(S[r][e], S[r][e + 1]);
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- gated RMSNorm over V per (token, head) ----
 #pragma unroll
@@ -336,13 +347,16 @@ constexpr int MTW = MC / (MT / 64);   // tokens staged per wave
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int GP = MC + 1;        // padded row stride of the Gram tiles
+constexpr int OP = D + 4;         // padded row stride of the read-outs
+constexpr int DP = MC + 4;        // padded row stride of the staged d
 
 struct MStage {
     float x[2 * MC][XP];          // rows t: k^_t, rows MC + t: q^_t (zero past the sub-chunk)
     float v[MC][D];
     float p[4][2 * MC][PP];       // per wave: S0 [k^|q^], [token column][value row]
     float gp[2][2][MC][GP];       // [K half][k^ or q^ columns][i][j]: partial k^_i . (k^|q^)_j
-    float o[MC][D];               // the read-outs, until the next sub-chunk's products ran
+    float o[MC][OP];              // the read-outs, until the next sub-chunk's products ran
+    float dd[4][32][DP];          // per wave: d, [value row][token], for the read-out products
     float akk[MC][MC];            // [t][i]: e^{G_t-G_i} k^_i.k^_t for i < t, else 0
     float bkq[MC][MC];            // [t][i]: e^{G_t-G_i} k^_i.q^_t for i <= t, else 0
     float gam[MC];                // e^{G_t}
@@ -350,33 +364,58 @@ struct MStage {
     float g[MC];                  // log alpha_t (0 past the sub-chunk)
     float G[MC];                  // running sums of g: G_t = g_0 + ... + g_t
     float beta[MC];               // (0 past the sub-chunk)
+    int32_t rows[2][MC];          // token rows of the current / previous sub-chunk
 };
 
 template <int ACT>
 struct MRaw {
     typename Pair<ACT>::raw q[MTW], k[MTW], v[MTW], z[MTW];
-    uint32_t a[MTW], b[MTW];
-    int64_t row[MTW];
+    uint32_t a, b;     // the gates of token pos + wave + 4 (lane % MTW) ...
+    int32_t row;       // ... and its row (rows fit 32 bits: they come from int32 offsets)
 };
 
-// Tokens of one sub-chunk for this wave: t = wave + 4 i.
+// The element idx of an activation tensor (idx wave-uniform: a scalar address).
+template <int ACT>
+__device__ __forceinline__ const void* elem_at(const void* base, int64_t idx)
+{
+    return static_cast<const char*>(base) + idx * (ACT == GDN_F32 ? 4 : 2);
+}
+
+// Tokens of one sub-chunk for this wave: t = wave + 4 i.  The row and head
+// offsets are wave-uniform; only the lane's pair offset is per lane.
 template <int ACT>
 __device__ __forceinline__ void issue_sub(const PParams& p, int64_t c0, int L, int pos,
                                           int wave, int lane, int h, int kh, MRaw<ACT>& r)
 {
+    const uint32_t e = 2u * static_cast<uint32_t>(lane);
+    // the token index map is read-only here: scalar loads, which the vector
+    // loads below need not wait behind
+    using cint = const __attribute__((address_space(4))) int32_t;
+    cint* tix = (cint*)(p.tix);
+    int64_t rows[MTW];
 #pragma unroll
     for (int i = 0; i < MTW; ++i) {
         const int t = pos + wave + 4 * i;
         const int tt = t < L ? t : L - 1;
-        const int64_t row = p.tix ? static_cast<int64_t>(p.tix[c0 + tt]) : c0 + tt;
-        r.row[i] = row;
-        r.q[i] = load_pair_raw<ACT>(p.q, row * p.q_st + kh * p.q_sh + 2 * lane);
-        r.k[i] = load_pair_raw<ACT>(p.k, row * p.k_st + kh * p.k_sh + 2 * lane);
-        r.v[i] = load_pair_raw<ACT>(p.v, row * p.v_st + h * p.v_sh + 2 * lane);
-        r.z[i] = load_pair_raw<ACT>(p.z, row * p.z_st + h * p.z_sh + 2 * lane);
-        r.a[i] = load_one_raw<ACT>(p.a, row * p.a_st + h);
-        r.b[i] = load_one_raw<ACT>(p.b, row * p.b_st + h);
+        rows[i] = p.tix ? static_cast<int64_t>(tix[c0 + tt]) : c0 + tt;
     }
+#pragma unroll
+    for (int i = 0; i < MTW; ++i) {
+        const int64_t row = rows[i];
+        r.q[i] = load_pair_raw<ACT>(elem_at<ACT>(p.q, row * p.q_st + kh * p.q_sh), e);
+        r.k[i] = load_pair_raw<ACT>(elem_at<ACT>(p.k, row * p.k_st + kh * p.k_sh), e);
+        r.v[i] = load_pair_raw<ACT>(elem_at<ACT>(p.v, row * p.v_st + h * p.v_sh), e);
+        r.z[i] = load_pair_raw<ACT>(elem_at<ACT>(p.z, row * p.z_st + h * p.z_sh), e);
+    }
+    // one token's gates per lane (token pos + wave + 4 (lane % MTW)), not
+    // every token's in every lane
+    int64_t row = rows[0];
+#pragma unroll
+    for (int i = 1; i < MTW; ++i)
+        row = lane % MTW == i ? rows[i] : row;
+    r.row = static_cast<int32_t>(row);
+    r.a = load_one_raw<ACT>(p.a, row * p.a_st + h);
+    r.b = load_one_raw<ACT>(p.b, row * p.b_st + h);
 }
 
 // Tokens in the sub-chunk at pos: up to MC, never across a chunk end.
@@ -421,22 +460,35 @@ __device__ __forceinline__ void store4_state(char* base, size_t e, const float* 
 
 // Gated RMSNorm over V per (token, head) for this wave's tokens t = wave + 4 i
 // of a sub-chunk of n tokens, from its read-outs o.
-template <int OUT>
-__device__ __forceinline__ void epilogue(const PParams& p, const float (&o)[MC][D],
-                                         const float2 (&z)[MTW], const int64_t (&rows)[MTW],
-                                         int n, int wave, int lane, int h, float2 wn)
+template <int ACT, int OUT>
+__device__ __forceinline__ void epilogue(const PParams& p, const float (&o)[MC][OP],
+                                         const typename Pair<ACT>::raw (&zr)[MTW],
+                                         const int32_t (&rows)[MC], int n, int wave, int lane,
+                                         int h, float2 wn)
 {
+    static_assert(MTW == 4, "one four-way wave sum per sub-chunk");
+    float2 ov[MTW];
+    float ms[MTW];
+#pragma unroll
+    for (int i = 0; i < MTW; ++i) {
+        // (rows past the sub-chunk are summed too: each sum is kept apart
+        // from the others, and theirs go unused)
+        ov[i] = *reinterpret_cast<const float2*>(&o[wave + 4 * i][2 * lane]);
+        ms[i] = ov[i].x * ov[i].x + ov[i].y * ov[i].y;
+    }
+    sum64x4(ms[0], ms[1], ms[2], ms[3]);
 #pragma unroll
     for (int i = 0; i < MTW; ++i) {
         const int t = wave + 4 * i;
         if (t < n) {
-            const float2 ov = *reinterpret_cast<const float2*>(&o[t][2 * lane]);
-            const float ms = sum64(ov.x * ov.x + ov.y * ov.y) * (1.0f / D);
-            const float rr = frsqrt(ms + p.norm_eps);
-            const float gx = z[i].x * sigmoid_fast(z[i].x);
-            const float gy = z[i].y * sigmoid_fast(z[i].y);
-            const float2 y = make_float2(ov.x * rr * wn.x * gx, ov.y * rr * wn.y * gy);
-            store_pair<OUT>(p.out, rows[i] * p.o_st + h * p.o_sh + 2 * lane, y);
+            const float rr = frsqrt(ms[i] * (1.0f / D) + p.norm_eps);
+            const float2 z = unpack_pair<ACT>(zr[i]);
+            const float gx = z.x * sigmoid_fast(z.x);
+            const float gy = z.y * sigmoid_fast(z.y);
+            const float2 y =
+                make_float2(ov[i].x * rr * wn.x * gx, ov[i].y * rr * wn.y * gy);
+            store_pair<OUT>(p.out, static_cast<int64_t>(rows[t]) * p.o_st + h * p.o_sh + 2 * lane,
+                            y);
         }
     }
 }
@@ -449,7 +501,9 @@ gdn_prefill_mma_kernel(const PParams p)
     __shared__ __attribute__((aligned(16))) MStage sm;
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    // wave-uniform, and known to be: the token rows and their addresses are then
+    // scalar arithmetic
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int lc = lane & 31;
     const int lh = lane >> 5;
@@ -481,63 +535,86 @@ gdn_prefill_mma_kernel(const PParams p)
     const size_t tile = static_cast<size_t>(D) * D;
     char* sbase = static_cast<char*>(p.pool) + (static_cast<size_t>(slot) * p.HV + h) * tile * ESZ;
     const int vrow = 32 * wave + lc;
+    // (every load issued, then the zero state selected, so that the 16 loads
+    // are in flight together)
     f32x16 S[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            float f[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-            if (init)
-                load4_state<ST>(sbase, static_cast<size_t>(vrow) * D + 32 * kb + 8 * q + 4 * lh, f);
+            float f[4];
+            load4_state<ST>(sbase, static_cast<size_t>(vrow) * D + 32 * kb + 8 * q + 4 * lh, f);
 #pragma unroll
             for (int m = 0; m < 4; ++m)
-                S[kb][4 * q + m] = f[m];
+                S[kb][4 * q + m] = init ? f[m] : 0.0f;
         }
 
     const float A = -expf(p.A_log[h]);
     const float dtb = p.dt_bias[h];
-    const float2 wn = *reinterpret_cast<const float2*>(p.norm_weight + 2 * lane);
+    float2 wn = *reinterpret_cast<const float2*>(p.norm_weight + 2 * lane);
+    // Complete these loads before the loop: a load still pending at the loop
+    // entry makes its uses inside the loop wait, conservatively, for the
+    // activation loads of the sub-chunk ahead as well.
+    asm volatile("" : "+v"(wn.x), "+v"(wn.y));
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            asm volatile("" : "+v"(S[kb][r]));
 
     // The gated RMSNorm of a sub-chunk runs while the next sub-chunk's
     // matrix products do: its tokens' rows, z and count stay in registers.
-    float2 zc[MTW];
-    int64_t rc[MTW];
-    int nprev = 0;
+    typename Pair<ACT>::raw zc[MTW];
+    int nprev = 0, par = 0;
+    // The activations of a sub-chunk are loaded while the previous one is
+    // processed: issued right after its staging, in every iteration (the
+    // positions clamp to the last row), so that they land in the registers
+    // the next iteration reads.
+    MRaw<ACT> raw;
+    issue_sub<ACT>(p, c0, L, 0, wave, lane, h, kh, raw);
     for (int pos = 0; pos < L;) {
         const int n = sub_len(pos, L, p.chunk);
         const int next = pos + n;
-        MRaw<ACT> raw;
-        issue_sub<ACT>(p, c0, L, pos, wave, lane, h, kh, raw);
-        float2 zn[MTW];
-        int64_t rn[MTW];
+        typename Pair<ACT>::raw zn[MTW];
 
         // ---- stage: normalised k and q, v, gates; z stays in registers ----
+        float nq[MTW], nk[MTW];
+#pragma unroll
+        for (int i = 0; i < MTW; ++i) {
+            const float2 qv = unpack_pair<ACT>(raw.q[i]);
+            const float2 kv = unpack_pair<ACT>(raw.k[i]);
+            nq[i] = qv.x * qv.x + qv.y * qv.y;
+            nk[i] = kv.x * kv.x + kv.y * kv.y;
+        }
+        sum64x4(nq[0], nq[1], nq[2], nq[3]);
+        sum64x4(nk[0], nk[1], nk[2], nk[3]);
 #pragma unroll
         for (int i = 0; i < MTW; ++i) {
             const int t = wave + 4 * i;
             const bool live = t < n;
             const float2 qv = unpack_pair<ACT>(raw.q[i]);
             const float2 kv = unpack_pair<ACT>(raw.k[i]);
-            const float nq = sum64(qv.x * qv.x + qv.y * qv.y);
-            const float nk = sum64(kv.x * kv.x + kv.y * kv.y);
-            const float rk = live ? frsqrt(nk + 1e-6f) : 0.0f;
-            const float rq = live ? p.scale * frsqrt(nq + 1e-6f) : 0.0f;
+            const float rk = live ? frsqrt(nk[i] + 1e-6f) : 0.0f;
+            const float rq = live ? p.scale * frsqrt(nq[i] + 1e-6f) : 0.0f;
             const float2 vv = unpack_pair<ACT>(raw.v[i]);
-            zn[i] = unpack_pair<ACT>(raw.z[i]);
-            rn[i] = raw.row[i];
+            zn[i] = raw.z[i];
             *reinterpret_cast<float2*>(&sm.x[t][2 * lane]) =
                 live ? make_float2(kv.x * rk, kv.y * rk) : make_float2(0.0f, 0.0f);
             *reinterpret_cast<float2*>(&sm.x[MC + t][2 * lane]) =
                 live ? make_float2(qv.x * rq, qv.y * rq) : make_float2(0.0f, 0.0f);
             *reinterpret_cast<float2*>(&sm.v[t][2 * lane]) =
                 live ? vv : make_float2(0.0f, 0.0f);
-            if (lane == 0) {
-                const float x = unpack_one<ACT>(raw.a[i]) + dtb;
-                sm.g[t] = live ? A * softplus_fast(x) : 0.0f;
-                sm.beta[t] = live ? sigmoid_fast(unpack_one<ACT>(raw.b[i])) : 0.0f;
-            }
         }
-        __syncthreads();
+        if (lane < MTW) {
+            const int t = wave + 4 * lane;
+            const bool live = t < n;
+            const float x = unpack_one<ACT>(raw.a) + dtb;
+            sm.g[t] = live ? A * softplus_fast(x) : 0.0f;
+            sm.beta[t] = live ? sigmoid_fast(unpack_one<ACT>(raw.b)) : 0.0f;
+            sm.rows[par][t] = raw.row;
+        }
+        issue_sub<ACT>(p, c0, L, next, wave, lane, h, kh, raw);
+        lds_barrier();
 
         // ---- S0 [k^ | q^] and this wave's share of the Gram matrix.  The
         // matrix phases run at raised wave priority, so that the other block
@@ -577,12 +654,10 @@ gdn_prefill_mma_kernel(const PParams p)
         }
         __builtin_amdgcn_s_setprio(0);
         // the previous sub-chunk's gated RMSNorm, while the products run
-        epilogue<OUT>(p, sm.o, zc, rc, nprev, wave, lane, h, wn);
+        epilogue<ACT, OUT>(p, sm.o, zc, sm.rows[par ^ 1], nprev, wave, lane, h, wn);
 #pragma unroll
-        for (int i = 0; i < MTW; ++i) {
+        for (int i = 0; i < MTW; ++i)
             zc[i] = zn[i];
-            rc[i] = rn[i];
-        }
         nprev = n;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -592,7 +667,7 @@ gdn_prefill_mma_kernel(const PParams p)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             sm.gp[wave >> 1][gcol][4 * lq + r][l16] = Gm[r];
-        __syncthreads();
+        lds_barrier();
 
         // ---- decay-weighted Gram coefficients (one (i, t) pair per thread) ----
         {
@@ -608,10 +683,10 @@ gdn_prefill_mma_kernel(const PParams p)
                 sm.wend[t] = fexp(Ge - Gt);
             }
         }
-        __syncthreads();
+        lds_barrier();
 
-        // ---- the triangular solve for d, and the read-outs: value row
-        // 32 wave + lc per lane; the lane halves split the read-outs ----
+        // ---- the triangular solve for d: value row 32 wave + lc per lane
+        // (both lane halves) ----
         // Right-looking: once d_i is known it is folded into every later
         // accumulator, which keeps each sum in ascending i (the same bits as
         // summing row by row) and leaves only one FMA per step on the chain
@@ -627,14 +702,33 @@ gdn_prefill_mma_kernel(const PParams p)
             for (int t = i + 1; t < MC; ++t)
                 acc[t] = fmaf(sm.akk[t][i], d[i], acc[t]);
         }
+        // ---- the read-outs O = diag(e^G) (S0 q^) + Bkq D on the 16 x 16 x 4
+        // form: token rows x this wave's value rows, two tiles of 16.  Step
+        // s takes token i = 4 (lane / 16) + s of the contraction.  d reaches
+        // the operand layout through LDS; only this wave reads its rows, and
+        // one wave's LDS accesses complete in order. ----
 #pragma unroll
-        for (int tt = 0; tt < MC / 2; ++tt) {
-            const int t = tt + (MC / 2) * lh;
-            float o = sm.gam[t] * sm.p[wave][MC + t][lc];
+        for (int m = 0; m < MC; m += 4)      // both lane halves write the same values
+            *reinterpret_cast<float4*>(&sm.dd[wave][lc][m]) =
+                make_float4(d[m], d[m + 1], d[m + 2], d[m + 3]);
+        {
+            const float4 a4 = *reinterpret_cast<const float4*>(&sm.bkq[l16][4 * lq]);
 #pragma unroll
-            for (int i = 0; i < MC; ++i)
-                o = fmaf(sm.bkq[t][i], d[i], o);
-            sm.o[t][vrow] = o;
+            for (int tile = 0; tile < 2; ++tile) {
+                const int vr = 16 * tile + l16;
+                const float4 b4 = *reinterpret_cast<const float4*>(&sm.dd[wave][vr][4 * lq]);
+                f32x4 c;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    c[j] = sm.gam[4 * lq + j] * sm.p[wave][MC + 4 * lq + j][vr];
+                c = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.x, b4.x, c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.y, b4.y, c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.z, b4.z, c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.w, b4.w, c, 0, 0, 0);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    sm.o[4 * lq + j][32 * wave + vr] = c[j];
+            }
         }
 
         // ---- S <- e^{G_end} S + D' K^T ----
@@ -666,11 +760,12 @@ gdn_prefill_mma_kernel(const PParams p)
                     S[kb][r + 1] = x1;
                 }
         }
-        __syncthreads();
+        lds_barrier();
 
         pos = next;
+        par ^= 1;
     }
-    epilogue<OUT>(p, sm.o, zc, rc, nprev, wave, lane, h, wn);
+    epilogue<ACT, OUT>(p, sm.o, zc, sm.rows[par ^ 1], nprev, wave, lane, h, wn);
 
     // ---- the final state, rounded once, written once ----
 #pragma unroll
