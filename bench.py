@@ -296,9 +296,10 @@ def timing_fields(gpu_ms, kern_ms, steps):
 def traffic_ceilings(kw, pools, alg_bytes, args, stream, dev):
     """What the memory system delivers for the timed launch's traffic: the
     same launches with no arithmetic (gdn_traffic_pattern: same grid, unit
-    mapping, metadata and blocks per CU, the same bytes moved, the same pools
-    cycled), and a plain device copy of the same byte count (half read, half
-    written), with buffers cycled over at least 2 GiB.  Both are timed like
+    mapping and metadata, the same bytes moved, the same pools cycled), at
+    the kernel's blocks per CU and at 1, 2, 3 and 4, the fastest taken as the
+    ceiling; and a plain device copy of the same byte count (half read, half
+    written), with buffers cycled over at least 2 GiB.  All are timed like
     the kernel.  The pattern launches overwrite the pools' written slots with
     copies of the rewind tiles, so they run after the kernel's timing."""
     import torch
@@ -307,12 +308,14 @@ def traffic_ceilings(kw, pools, alg_bytes, args, stream, dev):
 
     pk = dict(kw)
     pk["out"] = torch.empty_like(kw["out"])
+    shapes = {}
+    for bpc in (0, 1, 2, 3, 4):
+        def pattern(i):
+            pk["state"] = pools[i % len(pools)]
+            ops.traffic_pattern(**pk, blocks_per_cu=bpc)
 
-    def pattern(i):
-        pk["state"] = pools[i % len(pools)]
-        ops.traffic_pattern(**pk)
-
-    p_ms, _, _, _ = time_steps(pattern, args.steps, args.warmup, stream)
+        shapes[bpc], _, _, _ = time_steps(pattern, args.steps, args.warmup, stream)
+    p_ms = min(shapes.values())
     n = max(1, alg_bytes // 2)
     pairs = max(2, -(-MIN_CYCLED_POOL_BYTES // (2 * n)))
     bufs = [(torch.empty(n, dtype=torch.uint8, device=dev).fill_(1),
@@ -326,6 +329,8 @@ def traffic_ceilings(kw, pools, alg_bytes, args, stream, dev):
     del bufs
     p_s, c_s = p_ms / args.steps * 1e-3, c_ms / args.steps * 1e-3
     return {"ceiling_gbs": alg_bytes / p_s / 1e9, "ceiling_avg_us": p_s * 1e6,
+            "ceiling_as_kernel_us": shapes[0] / args.steps * 1e3,
+            "ceiling_blocks_per_cu": min(shapes, key=shapes.get),
             "copy_gbs": 2 * n / c_s / 1e9, "copy_avg_us": c_s * 1e6}
 
 

@@ -15,7 +15,10 @@
  *
  * Arguments, ownership, errors and the safety net are those of
  * gdn_mixed_decode_update (include/gdn_spec.h); with num_seqs == 0 the
- * single-token entries take their rows through non_spec_token_indx.  The
+ * single-token entries take their rows through non_spec_token_indx.
+ * blocks_per_cu: 0 runs as many blocks per CU as the update kernel would;
+ * 1..8 runs that many instead (a sweep of launch shapes for the same
+ * traffic); anything else is GDN_ERR_INVALID.  The
  * pool's written slots receive copies of the rewind tiles and `out` receives
  * meaningless bits: run it on scratch copies.  One kernel on `stream`, no
  * allocation, no synchronisation.
@@ -35,7 +38,7 @@ gdn_status gdn_traffic_pattern(const gdn_layer* layer, const gdn_state_pool* poo
                                const int32_t* num_accepted_tokens,
                                const int32_t* spec_token_indx, const int32_t* state_indices,
                                int32_t num_tokens, const int32_t* non_spec_token_indx,
-                               hipStream_t stream);
+                               int32_t blocks_per_cu, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -85,6 +85,7 @@ struct KParams {
     int64_t num_ns;           // single-token entries of a mixed launch (0: pure spec)
     int32_t spec_stride;
     int32_t max_writes;       // host bound on slot writes per unit (launch planning only)
+    int32_t pattern_blocks_per_cu;   // traffic pattern only: 0 = as the update kernel
 };
 
 // ---- the kernel ------------------------------------------------------------
@@ -705,21 +706,24 @@ __global__ void __launch_bounds__(NTHREADS) gdn_traffic_kernel(const KParams p)
     }
 }
 
-// Blocks per CU of the kernel whose traffic the pattern reproduces, and the
-// dynamic LDS that gives the pattern kernel (whose registers would allow
-// more) the same count.
+// Blocks per CU of the kernel whose traffic the pattern reproduces (or
+// `blocks_per_cu` when positive), and the dynamic LDS that gives the pattern
+// kernel (whose registers would allow more) that count.
 template <int A, int S, int O, bool SPEC>
-hipError_t traffic_lds(const KParams& p, size_t* lds)
+hipError_t traffic_lds(const KParams& p, int blocks_per_cu, size_t* lds)
 {
-    size_t real_lds = 0;
-    hipError_t e = plan_lds<SPEC ? MAXT : 1>(p.max_writes, S, &real_lds);
-    if (e != hipSuccess)
-        return e;
-    int n = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &n, reinterpret_cast<const void*>(&gdn_update_kernel<A, S, O, SPEC>), NTHREADS, real_lds);
-    if (e != hipSuccess)
-        return e;
+    hipError_t e;
+    int n = blocks_per_cu;
+    if (n <= 0) {
+        size_t real_lds = 0;
+        if ((e = plan_lds<SPEC ? MAXT : 1>(p.max_writes, S, &real_lds)) != hipSuccess)
+            return e;
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n, reinterpret_cast<const void*>(&gdn_update_kernel<A, S, O, SPEC>), NTHREADS,
+            real_lds);
+        if (e != hipSuccess)
+            return e;
+    }
     DeviceInfo d;
     if ((e = device_info(&d)) != hipSuccess)
         return e;
@@ -736,7 +740,7 @@ template <int A, int S, int O, bool SPEC>
 hipError_t launch_traffic_typed(const KParams& p, int64_t grid, hipStream_t stream)
 {
     size_t lds = 0;
-    hipError_t e = traffic_lds<A, S, O, SPEC>(p, &lds);
+    hipError_t e = traffic_lds<A, S, O, SPEC>(p, p.pattern_blocks_per_cu, &lds);
     if (e != hipSuccess)
         return e;
     KParams args = p;
@@ -939,7 +943,8 @@ extern "C" gdn_status gdn_traffic_pattern(const gdn_layer* layer, const gdn_stat
                                           const int32_t* num_accepted_tokens,
                                           const int32_t* spec_token_indx,
                                           const int32_t* state_indices, int32_t num_tokens,
-                                          const int32_t* non_spec_token_indx, hipStream_t stream)
+                                          const int32_t* non_spec_token_indx,
+                                          int32_t blocks_per_cu, hipStream_t stream)
 {
     gdn::clear_error();
     gdn_status st;
@@ -965,8 +970,11 @@ extern "C" gdn_status gdn_traffic_pattern(const gdn_layer* layer, const gdn_stat
     if (grid > 0x7fffffffLL)
         return gdn::fail(GDN_ERR_INVALID, "(num_seqs + num_tokens) * num_v_heads exceeds the "
                                           "grid limit");
+    if (blocks_per_cu < 0 || blocks_per_cu > 8)
+        return gdn::fail(GDN_ERR_INVALID, "blocks_per_cu %d outside 0..8", blocks_per_cu);
     KParams p = make_params(layer, pool);
     p.spec_stride = spec_stride;
+    p.pattern_blocks_per_cu = blocks_per_cu;
     if (num_seqs == 0) {
         // the single-token launch of gdn_decode_update
         p.state_idx = state_indices;

@@ -120,7 +120,7 @@ SIGNATURES = {
     "gdn_conv_abi_struct_sizes": (None, [ctypes.POINTER(ctypes.c_size_t)] * 2),
     "gdn_traffic_pattern": (ctypes.c_int, [ctypes.POINTER(GdnLayer),
                                            ctypes.POINTER(GdnStatePool), _VP, _I32, _I32, _VP,
-                                           _I32, _VP, _VP, _VP, _I32, _VP, _VP]),
+                                           _I32, _VP, _VP, _VP, _I32, _VP, _I32, _VP]),
 }
 
 
@@ -392,13 +392,14 @@ def traffic_pattern(q, k, v, z, a, b, A_log, dt_bias, norm_weight, state, *,
                     spec_cu_seqlens=None, spec_state_indices=None, num_accepted_tokens=None,
                     spec_token_indx=None, non_spec_state_indices=None,
                     non_spec_token_indx=None, out=None, scale=None, norm_eps=1e-5,
-                    max_q_len=MAX_DRAFT_TOKENS, single_launch=True):
+                    max_q_len=MAX_DRAFT_TOKENS, single_launch=True, blocks_per_cu=0):
     """The HBM traffic of the forward_core launch with the same arguments and
     no arithmetic (gdn_traffic_pattern, include/gdn_bench.h): a measurement
     of the memory system's ceiling for that traffic.  Overwrites the written
     slots of ``state`` with copies of the rewind tiles and ``out`` with
     meaningless bits.  ``single_launch`` is accepted for symmetry with
-    forward_core; a mixed batch is always one launch here."""
+    forward_core; a mixed batch is always one launch here.  ``blocks_per_cu``
+    > 0 replaces the kernel's blocks per CU."""
     lib = load_library()
     if out is None:
         out = torch.zeros_like(z)
@@ -417,7 +418,8 @@ def traffic_pattern(q, k, v, z, a, b, A_log, dt_bias, norm_weight, state, *,
     _check(lib.gdn_traffic_pattern(ctypes.byref(layer), ctypes.byref(pool), _ptr(cu), B,
                                    int(max_q_len), _ptr(si), si.shape[1] if has_spec else 1,
                                    _ptr(na), _ptr(st), _ptr(ns),
-                                   0 if ns is None else ns.shape[0], _ptr(nst), _stream(dev)))
+                                   0 if ns is None else ns.shape[0], _ptr(nst),
+                                   int(blocks_per_cu), _stream(dev)))
     return out
 
 

@@ -351,9 +351,12 @@ def test_traffic_pattern_argument_errors(lib):
     m = torch.zeros(16, dtype=torch.int32)
     p = ctypes.c_void_p(m.data_ptr())
     call = lambda L, B, maxq, ns: lib.gdn_traffic_pattern(   # noqa: E731
-        ctypes.byref(L), ctypes.byref(pool), p, B, maxq, p, 4, p, None, p, ns, None, None)
+        ctypes.byref(L), ctypes.byref(pool), p, B, maxq, p, 4, p, None, p, ns, None, 0, None)
     assert call(layer, 0, 4, 0) == 0                         # nothing to do
     assert call(layer, 1, 9, 0) == 2 and "exceeds" in ops.last_error()
     assert call(layer, -1, 4, 0) == 1
+    assert lib.gdn_traffic_pattern(ctypes.byref(layer), ctypes.byref(pool), p, 1, 4, p, 4, p,
+                                   None, p, 0, None, 9, None) == 1
+    assert "blocks_per_cu" in ops.last_error()
     layer.norm_weight = layer.norm_weight + 4
     assert call(layer, 1, 4, 0) == 1 and "norm_weight" in ops.last_error()
