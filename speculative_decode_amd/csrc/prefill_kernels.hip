@@ -328,9 +328,9 @@ gdn_prefill_kernel(const PParams p)
 // -- the token recurrence unrolled, the same values up to rounding order.
 // The products S0 [k^ | q^] (V x K by K x 2MC) and the update
 // S <- e^{G_end} S + D' K^T (D'_i = e^{G_end - G_i} d_i) run on
-// v_mfma_f32_32x32x2f32, the k^ rows of the Gram matrix on
-// v_mfma_f32_16x16x4f32; the MC x MC triangular solve for d runs on the
-// vector ALU, one value row per lane.
+// v_mfma_f32_32x32x2f32, the k^ rows of the Gram matrix and the read-outs
+// O = diag(e^G) S0 Q^ + Bkq D on v_mfma_f32_16x16x4f32; the MC x MC
+// triangular solve for d runs on the vector ALU, one value row per lane.
 //
 // Layout: wave w owns value rows v = 32w..32w+31.  The state is kept
 // transposed in the matrix-core accumulator layout: element r of tile kb in
@@ -428,7 +428,7 @@ __device__ __forceinline__ int sub_len(int pos, int L, int chunk)
 
 // Four consecutive state elements (k contiguous) to / from fp32.
 template <int ST>
-__device__ __forceinline__ void load4_state(const char* base, size_t e, float* f)
+__device__ __forceinline__ void load4_state(const char* base, uint32_t e, float* f)
 {
     if constexpr (ST == GDN_F32) {
         const uint4 w = *reinterpret_cast<const uint4*>(base + e * 4);
@@ -444,7 +444,7 @@ __device__ __forceinline__ void load4_state(const char* base, size_t e, float* f
 }
 
 template <int ST>
-__device__ __forceinline__ void store4_state(char* base, size_t e, const float* f)
+__device__ __forceinline__ void store4_state(char* base, uint32_t e, const float* f)
 {
     if constexpr (ST == GDN_F32) {
         *reinterpret_cast<uint4*>(base + e * 4) =
@@ -543,14 +543,17 @@ gdn_prefill_mma_kernel(const PParams p)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             float f[4];
-            load4_state<ST>(sbase, static_cast<size_t>(vrow) * D + 32 * kb + 8 * q + 4 * lh, f);
+            load4_state<ST>(sbase, static_cast<uint32_t>(vrow * D + 32 * kb + 8 * q + 4 * lh), f);
 #pragma unroll
             for (int m = 0; m < 4; ++m)
                 S[kb][4 * q + m] = init ? f[m] : 0.0f;
         }
 
-    const float A = -expf(p.A_log[h]);
-    const float dtb = p.dt_bias[h];
+    // head constants, wave-uniform: kept in scalar registers
+    const float A =
+        __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(-expf(p.A_log[h]))));
+    const float dtb =
+        __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(p.dt_bias[h])));
     float2 wn = *reinterpret_cast<const float2*>(p.norm_weight + 2 * lane);
     // Complete these loads before the loop: a load still pending at the loop
     // entry makes its uses inside the loop wait, conservatively, for the
@@ -684,6 +687,16 @@ gdn_prefill_mma_kernel(const PParams p)
             }
         }
         lds_barrier();
+        // the decay of S over the sub-chunk, ahead of the solve, whose
+        // dependent chain leaves issue slots free
+        {
+            const float ge = sm.gam[MC - 1];
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    S[kb][r] *= ge;
+        }
 
         // ---- the triangular solve for d: value row 32 wave + lc per lane
         // (both lane halves) ----
@@ -731,14 +744,8 @@ gdn_prefill_mma_kernel(const PParams p)
             }
         }
 
-        // ---- S <- e^{G_end} S + D' K^T ----
-        const float ge = sm.gam[MC - 1];
+        // ---- S <- (e^{G_end} S) + D' K^T ----
         __builtin_amdgcn_s_setprio(2);
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                S[kb][r] *= ge;
 #pragma unroll
         for (int s = 0; s < MC / 2; ++s) {
             const float b = lh ? sm.wend[2 * s + 1] * d[2 * s + 1] : sm.wend[2 * s] * d[2 * s];
@@ -776,7 +783,7 @@ gdn_prefill_mma_kernel(const PParams p)
 #pragma unroll
             for (int m = 0; m < 4; ++m)
                 f[m] = S[kb][4 * q + m];
-            store4_state<ST>(sbase, static_cast<size_t>(vrow) * D + 32 * kb + 8 * q + 4 * lh, f);
+            store4_state<ST>(sbase, static_cast<uint32_t>(vrow * D + 32 * kb + 8 * q + 4 * lh), f);
         }
 }
 
