@@ -39,9 +39,12 @@ __device__ __forceinline__ float sum64(float x)
 // Four wave sums at once, each wave-uniform: (x0, x1, x2, x3) are replaced by
 // their sums over the 64 lanes.  Two exchange steps inside each quad leave
 // lane l with the quad's partial sum of x_{l % 4}; two rotations finish the
-// sums of the lanes of a 16-lane row with the same l % 4, two swizzles across
-// rows the wave's, and lanes 0..3 hand out the four results.  About a third
-// of the instructions of four separate sum64 calls.
+// sums of the lanes of a 16-lane row with the same l % 4; the gfx950 row
+// swaps (v_permlane16_swap: rows 0/1 and 2/3; v_permlane32_swap: the two
+// halves), which stay in the vector ALU, add the rows; lanes 0..3 hand out
+// the four results.  Both operands of every add are the same two values in
+// every lane, so all lanes hold the same bits.  About a third of the
+// instructions of four separate sum64 calls.
 __device__ __forceinline__ void sum64x4(float& x0, float& x1, float& x2, float& x3)
 {
     const int lane = static_cast<int>(__lane_id());
@@ -53,8 +56,12 @@ __device__ __forceinline__ void sum64x4(float& x0, float& x1, float& x2, float& 
     e += dpp<0x4E>(hi ? a : c);       // quad_perm(2,3,0,1)
     e += dpp<0x124>(e);               // row_ror:4
     e += dpp<0x128>(e);               // row_ror:8
-    e += __shfl_xor(e, 16);
-    e += __shfl_xor(e, 32);
+    const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_int(e), __float_as_int(e),
+                                                      false, false);
+    e = __int_as_float(r16[0]) + __int_as_float(r16[1]);
+    const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_int(e), __float_as_int(e),
+                                                      false, false);
+    e = __int_as_float(r32[0]) + __int_as_float(r32[1]);
     x0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e), 0));
     x1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e), 1));
     x2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e), 2));
