@@ -359,6 +359,9 @@ def main():
                          "oracle is timed on (0: skip)")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the traffic-pattern and copy ceilings (gdn path)")
+    ap.add_argument("--issue-probe", action="store_true",
+                    help="time FP32 matrix and FP32 vector instruction streams on the same "
+                         "SIMDs, alone and together (gdn_issue_probe); one JSON line")
     args = ap.parse_args()
     if args.steps is None:
         args.steps = 1000 if args.workload == "tiny" else 200
@@ -384,6 +387,8 @@ def main():
         print(json.dumps({"calibrate_copy_bytes": n, "copies": args.steps}), flush=True)
         return
     ops.load_library()
+    if args.issue_probe:
+        return issue_probe(dev)
     args.workload = args.workload or DEFAULT_WORKLOAD[args.path]
     layers_given = args.layers
     args.layers = args.layers or DEFAULT_LAYERS[args.path]
@@ -539,6 +544,39 @@ def prefill_cpu_baseline(batch):
                       f"{batch.HV} v-heads) of the same workload; serial C, float64; "
                       f"{dt:.2f} s of the C call (marshalling outside the timer)",
             **host_info()}
+
+
+def issue_probe(dev, blocks=256, n_mfma=1000, n_valu=4000, reps=5):
+    """Whether a SIMD runs FP32 matrix and FP32 vector instructions of two
+    of its waves at the same time (gdn_issue_probe): one 512-thread block per
+    CU, waves 0-3 two chains of v_mfma_f32_32x32x2f32, waves 4-7 eight FP32
+    FMA chains, timed alone and together.  If "both" takes the sum of
+    the two, the SIMD issues them one after the other, and a kernel that
+    mixes them pays for both."""
+    import torch
+
+    from speculative_decode_amd import ops
+
+    out = torch.empty(blocks * 512, dtype=torch.float32, device=dev)
+    us = {}
+    for mode, name in ((1, "mfma_only_us"), (2, "valu_only_us"), (3, "both_us")):
+        ops.issue_probe(out, mode, n_mfma, n_valu)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            ops.issue_probe(out, mode, n_mfma, n_valu)
+        e1.record()
+        torch.cuda.synchronize()
+        us[name] = e0.elapsed_time(e1) * 1e3 / reps
+    mfma_flop = 4 * blocks * 2 * n_mfma * 32 * 32 * 2 * 2
+    valu_flop = 4 * blocks * n_valu * 64 * 8 * 2
+    line = {"probe": "FP32 matrix and vector instructions of two waves per SIMD",
+            "blocks": blocks, "n_mfma": n_mfma, "n_valu": n_valu, **us,
+            "sum_of_alone_us": us["mfma_only_us"] + us["valu_only_us"],
+            "mfma_tflops_alone": mfma_flop / us["mfma_only_us"] / 1e6,
+            "valu_tflops_alone": valu_flop / us["valu_only_us"] / 1e6}
+    print(json.dumps(line), flush=True)
 
 
 def bench_prefill(args, dev):

@@ -12,8 +12,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 SOURCES = [os.path.join(CSRC, f) for f in
-           ("gdn_kernels.hip", "conv_kernels.hip", "prefill_kernels.hip", "gdn_host.cpp",
-            "conv_host.cpp")]
+           ("gdn_kernels.hip", "conv_kernels.hip", "prefill_kernels.hip", "probe_kernels.hip",
+            "gdn_host.cpp", "conv_host.cpp")]
 LIB = os.path.join(HERE, "libgdn_spec.so")
 ARCH = "gfx950"
 

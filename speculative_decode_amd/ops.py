@@ -121,6 +121,7 @@ SIGNATURES = {
     "gdn_traffic_pattern": (ctypes.c_int, [ctypes.POINTER(GdnLayer),
                                            ctypes.POINTER(GdnStatePool), _VP, _I32, _I32, _VP,
                                            _I32, _VP, _VP, _VP, _I32, _VP, _I32, _VP]),
+    "gdn_issue_probe": (ctypes.c_int, [_VP, _I32, _I32, _I32, _I32, _VP]),
 }
 
 
@@ -421,6 +422,16 @@ def traffic_pattern(q, k, v, z, a, b, A_log, dt_bias, norm_weight, state, *,
                                    0 if ns is None else ns.shape[0], _ptr(nst),
                                    int(blocks_per_cu), _stream(dev)))
     return out
+
+
+def issue_probe(out: torch.Tensor, mode: int, n_mfma: int, n_valu: int):
+    """One launch of the FP32 matrix / vector issue probe (gdn_issue_probe,
+    include/gdn_bench.h) with out.numel() // 512 blocks of 512 threads."""
+    lib = load_library()
+    if out.dtype != torch.float32 or not out.is_contiguous() or out.numel() % 512:
+        raise ValueError("out must be a contiguous float32 tensor of blocks * 512 elements")
+    _check(lib.gdn_issue_probe(_ptr(out), out.numel() // 512, mode, n_mfma, n_valu,
+                               _stream(out.device)))
 
 
 def prefill_update(q, k, v, z, a, b, A_log, dt_bias, norm_weight, state, cu_seqlens,

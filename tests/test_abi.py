@@ -360,3 +360,16 @@ def test_traffic_pattern_argument_errors(lib):
     assert "blocks_per_cu" in ops.last_error()
     layer.norm_weight = layer.norm_weight + 4
     assert call(layer, 1, 4, 0) == 1 and "norm_weight" in ops.last_error()
+
+
+def test_issue_probe_argument_errors(lib):
+    """The issue probe checks its arguments on the host and enqueues nothing
+    when they fail (no device call here)."""
+    out = ctypes.c_void_p(0x1000)          # never dereferenced: every call fails first
+    assert lib.gdn_issue_probe(None, 1, 1, 1, 1, None) == 1 and "NULL" in ops.last_error()
+    assert lib.gdn_issue_probe(out, 1, 0, 1, 1, None) == 1 and "mode" in ops.last_error()
+    assert lib.gdn_issue_probe(out, 1, 4, 1, 1, None) == 1
+    assert lib.gdn_issue_probe(out, 0, 3, 1, 1, None) == 1 and "blocks" in ops.last_error()
+    assert lib.gdn_issue_probe(out, 65537, 3, 1, 1, None) == 1
+    assert lib.gdn_issue_probe(out, 1, 3, -1, 1, None) == 1 and "chain" in ops.last_error()
+    assert lib.gdn_issue_probe(out, 1, 3, 1, 1000001, None) == 1
