@@ -359,6 +359,8 @@ PREFILL_CONFIGS = {
                               chunk_size=64, seed=31),
     "prefill_ragged_b32": dict(lens=[64 * (1 + (7 * i) % 24) for i in range(32)], HK=4, HV=32,
                                act="bf16", state="bf16", chunk_size=64, init_frac=0.5, seed=32),
+    "prefill_b8_l2048": dict(lens=[2048] * 8, HK=4, HV=32, act="bf16", state="bf16",
+                             chunk_size=64, seed=33),
 }
 
 PREFILL_DESCRIPTIONS = {
@@ -368,6 +370,8 @@ PREFILL_DESCRIPTIONS = {
                          "BF16 state rounded every 64 tokens",
     "prefill_ragged_b32": "prefill B=32, 64..1536 tokens, HK=4 HV=32 K=V=128, bf16, BF16 "
                           "state, chunk 64, half with an initial state",
+    "prefill_b8_l2048": "prefill B=8 x 2048 tokens HK=4 HV=32 K=V=128, bf16 activations, "
+                        "BF16 state rounded every 64 tokens (one unit per CU)",
 }
 
 
