@@ -546,7 +546,7 @@ def prefill_cpu_baseline(batch):
             **host_info()}
 
 
-def issue_probe(dev, blocks=256, n_mfma=1000, n_valu=4000, reps=5):
+def issue_probe(dev, blocks=256, n_mfma=4000, n_valu=16000, reps=5):
     """Whether a SIMD runs FP32 matrix and FP32 vector instructions of two
     of its waves at the same time (gdn_issue_probe): one 512-thread block per
     CU, waves 0-3 two chains of v_mfma_f32_32x32x2f32, waves 4-7 eight FP32
@@ -575,7 +575,10 @@ def issue_probe(dev, blocks=256, n_mfma=1000, n_valu=4000, reps=5):
             "blocks": blocks, "n_mfma": n_mfma, "n_valu": n_valu, **us,
             "sum_of_alone_us": us["mfma_only_us"] + us["valu_only_us"],
             "mfma_tflops_alone": mfma_flop / us["mfma_only_us"] / 1e6,
-            "valu_tflops_alone": valu_flop / us["valu_only_us"] / 1e6}
+            "valu_tflops_alone": valu_flop / us["valu_only_us"] / 1e6,
+            # per SIMD, at the 2.4 GHz the peak figures assume
+            "mfma_cycles_each": us["mfma_only_us"] * 2400 / (2 * n_mfma),
+            "valu_cycles_each": us["valu_only_us"] * 2400 / (8 * n_valu)}
     print(json.dumps(line), flush=True)
 
 
