@@ -230,3 +230,35 @@ def test_fp8_state_saturates(dev, chunk):
     gp, go = check(b, dev)
     live = sorted(set(b.state_indices.tolist()))
     assert (gp[live].double().abs() == 448.0).sum() > 5000
+
+
+def _random_prefill(i):
+    """Configuration i of the randomized sweep (a fixed generator: the same
+    configurations every run)."""
+    r = np.random.default_rng(3000 + i)
+    HK = int(r.choice([1, 2, 4]))
+    HV = HK * int(r.choice([1, 2, 4]))
+    B = int(r.integers(1, 6))
+    lens = [int(x) for x in r.integers(0, 161, size=B)]
+    if sum(lens) == 0:
+        lens[0] = int(r.integers(1, 161))
+    dts = ["f32", "bf16", "f16"]
+    return dict(lens=lens, HK=HK, HV=HV, act=str(r.choice(dts)),
+                state=str(r.choice(dts + ["f8"])), out=str(r.choice(dts)),
+                chunk_size=int(r.choice([1, 5, 15, 16, 17, 32, 48, 64, 100])),
+                init_frac=float(r.choice([1.0, 0.5])), num_slots=B + int(r.integers(0, 4)),
+                seed=4000 + i), r
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_configurations(dev, i):
+    """Sixteen seeded random batches, each compared whole: 1-5 sequences of
+    0-160 tokens, GQA ratios 1-4, every activation, state (FP8 included) and
+    output dtype, chunk sizes on both sides of the chunkwise kernel's 16 and
+    not multiples of it, some sequences without an initial state, pools with
+    spare slots, half of them through a permuted token index."""
+    cfg, r = _random_prefill(i)
+    b = workloads.prefill_batch(**cfg)
+    if r.random() < 0.5 and b.n_tok > 1:
+        b.token_indx = torch.from_numpy(r.permutation(b.n_tok).astype(np.int32))
+    check(b, dev)
