@@ -233,3 +233,31 @@ def test_decode_entry_gathered(dev, dtype):
                                                                         dtype=b.x.dtype))
     assert torch.equal(cache.cpu(), oc)
     assert_out_close(out.cpu(), oo, list(range(n)), b.out_dtype)
+
+
+def _random_conv(i):
+    """Configuration i of the randomized sweep (a fixed generator)."""
+    r = np.random.default_rng(5000 + i)
+    B = int(r.integers(1, 7))
+    T = int(r.integers(1, 9))
+    width = int(r.integers(1, 5))
+    q_lens = [int(x) for x in r.integers(0, T + 1, size=B)]
+    if sum(q_lens) == 0:
+        q_lens[0] = T
+    C = int(r.choice([8, 24, 40, 512, 520, 1000, 1536, 37]))
+    dts = ["f32", "bf16", "f16"]
+    return dict(B=B, T=T, C=C, width=width,
+                state_len=max(width - 2 + T, width - 1) + int(r.integers(0, 3)),
+                dtype=str(r.choice(dts)), out=str(r.choice(dts)),
+                num_lines=B + int(r.integers(0, 4)), q_lens=q_lens, acc_lo=0, acc_hi=T,
+                bias=bool(r.integers(0, 2)), activation=str(r.choice(["silu", "none"])),
+                gather=bool(r.integers(0, 2)), seed=6000 + i)
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_configurations(dev, i):
+    """Sixteen seeded random batches, each compared whole: 1-6 sequences of
+    0-8 drafts, widths 1-4, channel counts on the vector and element-wise
+    paths, every input and output dtype, buffers longer than needed, bias and
+    activation on or off, half through a permuted gather index."""
+    check(workloads.conv_batch(**_random_conv(i)), dev)
