@@ -579,3 +579,22 @@ def test_traffic_pattern_moves_the_launch_bytes(dev, name):
     rows = processed_rows(b)
     other = [r for r in range(b.n_tok) if r not in set(rows)]
     assert (args["out"][other] == 0).all() if other else True
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_mixed_configurations(dev, i):
+    """Twelve seeded random mixed batches in one launch, each compared whole:
+    0-40 single tokens and 0-12 speculative sequences of 1-8 drafts in
+    random unit order (so the single-launch interleave sees every
+    proportion, one part empty included), GQA ratios 1-8 and every dtype."""
+    r = np.random.default_rng(7000 + i)
+    HK = int(r.choice([1, 2, 4]))
+    n_non_spec, n_spec = int(r.integers(0, 41)), int(r.integers(0, 13))
+    if n_non_spec + n_spec == 0:
+        n_spec = 1
+    dts = ["f32", "bf16", "f16"]
+    b = workloads.mixed_batch(n_non_spec=n_non_spec, n_spec=n_spec, T=int(r.integers(1, 9)),
+                              HK=HK, HV=HK * int(r.choice([1, 2, 4, 8])),
+                              act=str(r.choice(dts)), state=str(r.choice(dts + ["f8"])),
+                              out=str(r.choice(dts)), seed=8000 + i)
+    check_full(b, dev)
